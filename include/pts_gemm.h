@@ -1,0 +1,206 @@
+/*
+ * pts_gemm.h -- C ABI of the persistent-tile-scheduled bf16 GEMM for MI355X (gfx950).
+ *
+ * The library computes D = A * B for one problem or for a group of independent
+ * problems in ONE persistent kernel launch. A fixed set of resident
+ * workgroups ("workers") each loops over output tiles. Where a worker's next
+ * tile comes from is the schedule:
+ *
+ *   - static grid-stride: worker w takes tiles w, w+P, w+2P, ... (P workers).
+ *     This is the static persistent schedule of "Advanced scheduling: Cluster
+ *     Launch Control", section "Limits of the static persistent scheduler",
+ *     and the static persistent shape of the CUTLASS Task Scheduling page
+ *     "Schedules", section "Scheduling Shapes".
+ *   - dynamic work claiming: every tile, the first one included, is claimed
+ *     from one device-wide atomic counter. The claim for the next tile is
+ *     issued before the current tile is computed, and a claim that returns an
+ *     index >= the tile count ends the worker's loop; it never claims again.
+ *     This is the single-GPU analogue of the hardware work stealing in "Advanced
+ *     scheduling: Cluster Launch Control", sections "One CLC request" and
+ *     "Overlapping the request with the current computation".
+ *
+ * Both schedules run the same tile body (same loads, same MFMA order, same
+ * epilogue), so for identical inputs they write bit-identical D; only the
+ * source of the next tile coordinate differs ("Advanced scheduling: Cluster
+ * Launch Control", section "When to use CLC").
+ *
+ * Operand layouts (the only ones supported):
+ *   A: M x K, row-major,    A[i][k] = a[i * lda + k], bf16
+ *   B: K x N, column-major, B[k][j] = b[j * ldb + k], bf16
+ *   D: M x N, row-major,    D[i][j] = d[i * ldd + j], fp32 or bf16
+ * Products are exact and accumulate in fp32 (MFMA). bf16 output rounds the
+ * fp32 sum to nearest, ties to even.
+ *
+ * Memory: every pointer is device memory owned by the caller; the library
+ * never allocates, frees or reads host copies of operand data. A plan owns a
+ * few bytes of device memory of its own (tile metadata and the claim
+ * counters), allocated in gemm_plan_create and freed in gemm_plan_destroy.
+ *
+ * Streams: `stream` arguments are hipStream_t values passed as void*
+ * (NULL = the default stream). Every run is asynchronous on its stream.
+ *
+ * Threads and concurrency: a plan is not thread-safe, and one plan must not
+ * have two runs in flight at once (its claim counter is per plan); create one
+ * plan per concurrent stream instead. Runs of different plans may overlap.
+ *
+ * Errors: every call returns a gemm_status; gemm_last_error() returns a
+ * message for the most recent failure on the calling thread.
+ */
+#ifndef PTS_GEMM_H
+#define PTS_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_VALUE = 1, /* a NULL pointer, a bad size, stride or alignment */
+    GEMM_ERR_UNSUPPORTED = 2,   /* a layout, dtype, tile or group count the library does not build */
+    GEMM_ERR_OUT_OF_MEMORY = 3, /* the plan's own device memory could not be allocated */
+    GEMM_ERR_HIP = 4,           /* a HIP runtime call failed (launch, copy, device query) */
+    GEMM_ERR_TIMEOUT = 5        /* a bounded device-side wait ran out (probe kernel only) */
+} gemm_status;
+
+typedef enum { GEMM_DTYPE_BF16 = 0, GEMM_DTYPE_F32 = 1 } gemm_dtype;
+typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout;
+typedef enum { GEMM_SCHEDULE_STATIC = 0, GEMM_SCHEDULE_DYNAMIC = 1 } gemm_schedule;
+
+/* Largest group count one plan accepts: the per-problem operand pointers of a
+ * run travel in the kernel's argument block. */
+#define GEMM_MAX_GROUPS 64
+
+/* One problem. m, n, k >= 0 and each below 2^31. ld = 0 selects the packed
+ * value (lda = ldb = k, ldd = n). lda and ldb must be multiples of 8 (rows of
+ * A and columns of B start 16-byte aligned) and >= k; ldd >= n. */
+typedef struct {
+    int64_t m, n, k;
+    int64_t lda, ldb, ldd;
+} gemm_shape;
+
+/* Plan flags. */
+#define GEMM_FLAG_NONE 0u
+
+typedef struct {
+    int32_t group_count;       /* 1 = one GEMM; 2..GEMM_MAX_GROUPS = grouped, one launch */
+    const gemm_shape *shapes;  /* host array[group_count]; copied by gemm_plan_create */
+    int32_t layout_a;          /* GEMM_ROW_MAJOR */
+    int32_t layout_b;          /* GEMM_COL_MAJOR */
+    int32_t layout_d;          /* GEMM_ROW_MAJOR */
+    int32_t dtype_a;           /* GEMM_DTYPE_BF16 */
+    int32_t dtype_b;           /* GEMM_DTYPE_BF16 */
+    int32_t dtype_acc;         /* GEMM_DTYPE_F32 */
+    int32_t dtype_d;           /* GEMM_DTYPE_F32 or GEMM_DTYPE_BF16 */
+    int32_t tile_m, tile_n;    /* output tile; 0 = 256. Built: 256x256, 128x128, 64x64 */
+    int32_t schedule;          /* gemm_schedule */
+    int32_t num_workers;       /* 0 = one per compute unit times occupancy, capped at the tile count */
+    uint32_t flags;            /* GEMM_FLAG_* */
+} gemm_desc;
+
+typedef struct gemm_plan gemm_plan; /* opaque */
+
+/* Device pointers of one problem. a and b must be 16-byte aligned; d at
+ * least element aligned. A must be readable over (m-1)*lda + roundup(k, 8)
+ * elements and B over (n-1)*ldb + roundup(k, 8): the last row of A (column
+ * of B) is read in whole 16-byte chunks. Elements of D outside the m x n
+ * region (row padding up to ldd) are never written. */
+typedef struct {
+    const void *a;
+    const void *b;
+    void *d;
+} gemm_operands;
+
+/* Message for a status code (static storage). */
+const char *gemm_status_string(gemm_status status);
+
+/* Message describing the most recent failure on this thread ("" if none). */
+const char *gemm_last_error(void);
+
+/*
+ * Validate a descriptor and build a plan on the current HIP device.
+ * Everything checkable without the operand pointers is checked here (shapes,
+ * strides, layouts, dtypes, tile size, worker count); on any error *out_plan is
+ * set to NULL and nothing is allocated. The validation mirrors the pages'
+ * rule that mismatched pipeline configurations are rejected when the group is
+ * constructed (CUTLASS Task Scheduling page "Pipeline Groups", section "How
+ * member configs are merged").
+ */
+gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan);
+
+/*
+ * Run the plan: one persistent kernel launch on `stream` computing every
+ * problem of the plan. `ops` is a host array of desc.group_count operand sets.
+ * Returns GEMM_ERR_INVALID_VALUE for a NULL or misaligned pointer (nothing is
+ * launched), GEMM_ERR_HIP if the launch fails. Problems with m = 0 or n = 0
+ * write nothing; k = 0 writes zeros. The run must be on the device the plan
+ * was created on.
+ */
+gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream);
+
+/* Free the plan and its device memory. NULL is a no-op. The caller must
+ * ensure no run of the plan is still executing. */
+gemm_status gemm_plan_destroy(gemm_plan *plan);
+
+/* Tile count, worker count (grid size) and LDS bytes per workgroup of a plan.
+ * Any output pointer may be NULL. */
+gemm_status gemm_plan_query(const gemm_plan *plan, int64_t *num_tiles, int32_t *num_workers,
+                            int32_t *lds_bytes);
+
+/*
+ * Per-tile trace (test and benchmark use). After this call every run writes,
+ * into `device_buf`, one record per tile followed by one record per worker:
+ *
+ *   struct { int32 tile, worker, seq, group, row0, col0; uint32 hw_id, xcc_id;
+ *            uint64 t_start, t_end; }              -- 48 bytes, at index `tile`
+ *   struct { uint64 t_start, t_end; int32 tiles, worker; uint32 hw_id, xcc_id; }
+ *                                                  -- 32 bytes, at index `worker`
+ *
+ * Times are the 100 MHz device real-time counter; seq is the tile's position
+ * in its worker's sequence; hw_id is the wave's HW_ID register and xcc_id its
+ * XCC (chiplet) id. `bytes` must be >= 48 * num_tiles + 32 * num_workers.
+ * device_buf = NULL switches tracing off.
+ */
+gemm_status gemm_plan_set_trace(gemm_plan *plan, void *device_buf, size_t bytes);
+
+/*
+ * Read the plan's scheduler counters (synchronizes the device): out[0] the
+ * live claim counter (0 between dynamic runs), out[1] the live exit counter
+ * (0 between runs), out[2] the claim counter's final value in the last
+ * dynamic run (tiles + workers: every worker's loop ends on exactly one failed
+ * claim), out[3] the number of dynamic runs completed.
+ */
+gemm_status gemm_plan_read_counters(const gemm_plan *plan, uint32_t out[4]);
+
+/*
+ * Grid-stride int16 copy dst[i] = src[i] for 0 <= i < n, 16 bytes per lane per
+ * step ("Schedules", section "Domains": start = block * threads + thread,
+ * step = grid * threads, indices >= n untouched). Used as the concurrent
+ * HBM-bound load beside a GEMM. src and dst must be 16-byte aligned and must
+ * not overlap. num_blocks = 0 picks one block per compute unit times 4.
+ */
+gemm_status pts_copy_int16(const void *src, void *dst, int64_t n, int32_t num_blocks, void *stream);
+
+/*
+ * Scheduler probe: runs the tile scheduler alone, with `work_ns` of busy-wait
+ * standing in for each tile's work, one 64-thread workgroup per worker.
+ * out_tiles[w * max_per_worker + i] receives the i-th tile worker w processed
+ * and out_counts[w] how many; both are device arrays of num_workers rows.
+ * gate_worker >= 0 holds that worker back until all others have finished
+ * (bounded by spin_limit polls; on expiry out_status[0] = 1), which replays a
+ * worker that starts late. counters: device array of 4 uint32 zeroed by the
+ * caller before the first call (the dynamic counter resets itself at the end
+ * of every call). out_status: device array of 1 uint32.
+ */
+gemm_status pts_sched_probe(int32_t num_tiles, int32_t num_workers, int32_t schedule,
+                            int32_t gate_worker, int64_t work_ns, int64_t spin_limit,
+                            int32_t *out_tiles, int32_t *out_counts, int32_t max_per_worker,
+                            uint32_t *counters, uint32_t *out_status, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PTS_GEMM_H */

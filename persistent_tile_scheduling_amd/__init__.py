@@ -1,0 +1,267 @@
+"""Python binding of the persistent-tile-scheduled bf16 GEMM library.
+
+Argument marshalling only: every step of the GEMM runs in the HIP kernels of
+``_lib/libpts_gemm.so`` (built from ``csrc/`` by ``build.py``). The functions
+carry the C ABI's names (``include/pts_gemm.h``); ``Plan`` and ``gemm`` are
+small conveniences over them that take torch tensors for device memory.
+
+There is no fallback: importing this package raises if the HIP library has
+not been built, and every call raises ``GemmError`` on a non-OK status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so that the library binds to torch's HIP runtime
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_lib", "libpts_gemm.so")
+
+GEMM_OK = 0
+GEMM_ERR_INVALID_VALUE = 1
+GEMM_ERR_UNSUPPORTED = 2
+GEMM_ERR_OUT_OF_MEMORY = 3
+GEMM_ERR_HIP = 4
+GEMM_ERR_TIMEOUT = 5
+
+GEMM_DTYPE_BF16 = 0
+GEMM_DTYPE_F32 = 1
+GEMM_ROW_MAJOR = 0
+GEMM_COL_MAJOR = 1
+GEMM_SCHEDULE_STATIC = 0
+GEMM_SCHEDULE_DYNAMIC = 1
+GEMM_MAX_GROUPS = 64
+GEMM_FLAG_NONE = 0
+
+TILE_TRACE_BYTES = 48
+WORKER_TRACE_BYTES = 32
+
+
+class GemmShape(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldd", ctypes.c_int64)]
+
+
+class GemmDesc(ctypes.Structure):
+    _fields_ = [("group_count", ctypes.c_int32), ("shapes", ctypes.POINTER(GemmShape)),
+                ("layout_a", ctypes.c_int32), ("layout_b", ctypes.c_int32), ("layout_d", ctypes.c_int32),
+                ("dtype_a", ctypes.c_int32), ("dtype_b", ctypes.c_int32), ("dtype_acc", ctypes.c_int32),
+                ("dtype_d", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("schedule", ctypes.c_int32), ("num_workers", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class GemmOperands(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("d", ctypes.c_void_p)]
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"HIP library not built: {LIB_PATH} is missing "
+                          "(run persistent_tile_scheduling_amd/build.py or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    sig = {
+        "gemm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "gemm_last_error": (ctypes.c_char_p, []),
+        "gemm_plan_create": (ctypes.c_int, [ctypes.POINTER(GemmDesc), ctypes.POINTER(P)]),
+        "gemm_run": (ctypes.c_int, [P, ctypes.POINTER(GemmOperands), P]),
+        "gemm_plan_destroy": (ctypes.c_int, [P]),
+        "gemm_plan_query": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32),
+                                           ctypes.POINTER(ctypes.c_int32)]),
+        "gemm_plan_set_trace": (ctypes.c_int, [P, P, ctypes.c_size_t]),
+        "gemm_plan_read_counters": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_uint32)]),
+        "pts_copy_int16": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32, P]),
+        "pts_sched_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int64, ctypes.c_int64, P, P, ctypes.c_int32, P, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != GEMM_OK:
+        raise GemmError(status, _lib.gemm_last_error().decode() or gemm_status_string(status))
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        return t.data_ptr()
+    return int(t)
+
+
+# ---------------------------------------------------------------------------
+# C ABI, same names
+# ---------------------------------------------------------------------------
+
+def gemm_status_string(status: int) -> str:
+    return _lib.gemm_status_string(status).decode()
+
+
+def gemm_last_error() -> str:
+    return _lib.gemm_last_error().decode()
+
+
+def make_desc(shapes, dtype_d: int = GEMM_DTYPE_F32, tile=(0, 0), schedule: int = GEMM_SCHEDULE_STATIC,
+              num_workers: int = 0, flags: int = GEMM_FLAG_NONE, layouts=(GEMM_ROW_MAJOR, GEMM_COL_MAJOR,
+                                                                           GEMM_ROW_MAJOR),
+              dtypes=(GEMM_DTYPE_BF16, GEMM_DTYPE_BF16, GEMM_DTYPE_F32)):
+    """Build a ``gemm_desc``. ``shapes`` is a list of (m, n, k[, lda, ldb, ldd])."""
+    arr = (GemmShape * max(1, len(shapes)))()
+    for i, s in enumerate(shapes):
+        s = tuple(s) + (0,) * (6 - len(s))
+        arr[i] = GemmShape(*[int(v) for v in s])
+    d = GemmDesc(len(shapes), ctypes.cast(arr, ctypes.POINTER(GemmShape)), layouts[0], layouts[1], layouts[2],
+                 dtypes[0], dtypes[1], dtypes[2], dtype_d, tile[0], tile[1], schedule, num_workers, flags)
+    d._shapes_keepalive = arr
+    return d
+
+
+def gemm_plan_create(desc: GemmDesc) -> int:
+    out = ctypes.c_void_p()
+    _check(_lib.gemm_plan_create(ctypes.byref(desc), ctypes.byref(out)))
+    return out.value
+
+
+def gemm_run(plan: int, operands, stream=None) -> None:
+    """``operands``: list of (a, b, d) device pointers or tensors, one per problem."""
+    arr = (GemmOperands * max(1, len(operands)))()
+    for i, (a, b, d) in enumerate(operands):
+        arr[i] = GemmOperands(_ptr(a), _ptr(b), _ptr(d))
+    _check(_lib.gemm_run(ctypes.c_void_p(plan), arr, ctypes.c_void_p(_stream_handle(stream))))
+
+
+def gemm_plan_destroy(plan: int | None) -> None:
+    _check(_lib.gemm_plan_destroy(ctypes.c_void_p(plan)))
+
+
+def gemm_plan_query(plan: int) -> tuple[int, int, int]:
+    t, w, l = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.gemm_plan_query(ctypes.c_void_p(plan), ctypes.byref(t), ctypes.byref(w), ctypes.byref(l)))
+    return t.value, w.value, l.value
+
+
+def gemm_plan_set_trace(plan: int, device_buf, nbytes: int) -> None:
+    _check(_lib.gemm_plan_set_trace(ctypes.c_void_p(plan), ctypes.c_void_p(_ptr(device_buf)), nbytes))
+
+
+def gemm_plan_read_counters(plan: int) -> list[int]:
+    out = (ctypes.c_uint32 * 4)()
+    _check(_lib.gemm_plan_read_counters(ctypes.c_void_p(plan), out))
+    return list(out)
+
+
+def pts_copy_int16(src, dst, n: int, num_blocks: int = 0, stream=None) -> None:
+    _check(_lib.pts_copy_int16(ctypes.c_void_p(_ptr(src)), ctypes.c_void_p(_ptr(dst)), n, num_blocks,
+                               ctypes.c_void_p(_stream_handle(stream))))
+
+
+def pts_sched_probe(num_tiles: int, num_workers: int, schedule: int, gate_worker: int, work_ns: int,
+                    spin_limit: int, out_tiles, out_counts, max_per_worker: int, counters, out_status,
+                    stream=None) -> None:
+    _check(_lib.pts_sched_probe(num_tiles, num_workers, schedule, gate_worker, work_ns, spin_limit,
+                                ctypes.c_void_p(_ptr(out_tiles)), ctypes.c_void_p(_ptr(out_counts)),
+                                max_per_worker, ctypes.c_void_p(_ptr(counters)),
+                                ctypes.c_void_p(_ptr(out_status)), ctypes.c_void_p(_stream_handle(stream))))
+
+
+# ---------------------------------------------------------------------------
+# Conveniences over the C ABI
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """Owns one ``gemm_plan``. ``shapes``: list of (m, n, k[, lda, ldb, ldd])."""
+
+    def __init__(self, shapes, out_dtype=torch.float32, tile=(0, 0), schedule: str | int = "static",
+                 num_workers: int = 0):
+        if isinstance(schedule, str):
+            schedule = {"static": GEMM_SCHEDULE_STATIC, "dynamic": GEMM_SCHEDULE_DYNAMIC}[schedule]
+        dtype_d = {torch.float32: GEMM_DTYPE_F32, torch.bfloat16: GEMM_DTYPE_BF16}[out_dtype]
+        self.shapes = [tuple(s) for s in shapes]
+        self.out_dtype = out_dtype
+        self.schedule = schedule
+        self.desc = make_desc(self.shapes, dtype_d, tile, schedule, num_workers)
+        self.handle = gemm_plan_create(self.desc)
+        self.num_tiles, self.num_workers, self.lds_bytes = gemm_plan_query(self.handle)
+
+    def run(self, operands, stream=None) -> None:
+        gemm_run(self.handle, operands, stream)
+
+    def counters(self) -> list[int]:
+        return gemm_plan_read_counters(self.handle)
+
+    def trace_bytes(self) -> int:
+        return TILE_TRACE_BYTES * self.num_tiles + WORKER_TRACE_BYTES * self.num_workers
+
+    def set_trace(self, buf) -> None:
+        gemm_plan_set_trace(self.handle, buf, 0 if buf is None else buf.numel() * buf.element_size())
+
+    def close(self) -> None:
+        if self.handle:
+            gemm_plan_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def decode_trace(buf: torch.Tensor, num_tiles: int, num_workers: int):
+    """Split a trace buffer (any dtype, on any device) into numpy record arrays."""
+    import numpy as np
+    raw = buf.detach().cpu().contiguous().view(torch.uint8).numpy()
+    tile_dt = np.dtype([("tile", "<i4"), ("worker", "<i4"), ("seq", "<i4"), ("group", "<i4"), ("row0", "<i4"),
+                        ("col0", "<i4"), ("hw_id", "<u4"), ("xcc_id", "<u4"), ("t_start", "<u8"),
+                        ("t_end", "<u8")])
+    worker_dt = np.dtype([("t_start", "<u8"), ("t_end", "<u8"), ("tiles", "<i4"), ("worker", "<i4"),
+                          ("hw_id", "<u4"), ("xcc_id", "<u4")])
+    nt = TILE_TRACE_BYTES * num_tiles
+    tiles = raw[:nt].view(tile_dt)
+    workers = raw[nt:nt + WORKER_TRACE_BYTES * num_workers].view(worker_dt)
+    return tiles, workers
+
+
+def gemm(a: torch.Tensor, b: torch.Tensor, out_dtype=torch.float32, schedule="static", tile=(0, 0),
+         num_workers: int = 0, out: torch.Tensor | None = None, k: int | None = None) -> torch.Tensor:
+    """D = A . B for A (m x lda, row-major) and B given as (n x ldb) = B^T row-major.
+
+    ``k`` defaults to ``a.shape[1]`` (no padding). Builds a one-shot plan.
+    """
+    m, lda = a.shape
+    n, ldb = b.shape
+    kk = lda if k is None else k
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    with Plan([(m, n, kk, lda, ldb, out.stride(0))], out.dtype, tile, schedule, num_workers) as p:
+        p.run([(a, b, out)])
+    return out

@@ -1,0 +1,85 @@
+// Auxiliary kernels: the grid-stride int16 copy and the scheduler probe.
+#pragma once
+
+#include "common.h"
+#include "scheduler.h"
+
+namespace pts {
+
+// Grid-stride copy ("Schedules" page, section "Domains": thread index
+// start = block * threads + thread, stride = grid * threads; an index is
+// copied only while it is below the element count). Each lane moves 16 bytes
+// (8 int16) per step; the n % 8 tail elements go to the first threads.
+__global__ __launch_bounds__(256) void copy_int16_kernel(const int4 *__restrict__ src, int4 *__restrict__ dst,
+                                                         int64_t nvec, const int16_t *__restrict__ src16,
+                                                         int16_t *__restrict__ dst16, int64_t n)
+{
+    const int64_t start = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = start; i < nvec; i += step)
+        dst[i] = src[i];
+    const int64_t tail = nvec * 8 + start;
+    if (start < 8 && tail < n)
+        dst16[tail] = src16[tail];
+}
+
+// Scheduler probe: the tile scheduler of the GEMM kernel with a fixed busy
+// wait standing in for a tile's work. One wave per worker.
+//
+// out_tiles[w * max_per_worker + i]: i-th tile of worker w; out_counts[w]:
+// how many. gate_worker (if >= 0) first waits until every other worker has
+// finished -- the late-starting worker of "Advanced scheduling: Cluster Launch
+// Control", section "Limits of the static persistent scheduler". The wait
+// polls at most spin_limit times; on expiry status[0] = 1 and the worker goes
+// on, so the kernel always ends.
+//
+// counters: [0..3] as in TileScheduler, [4] workers done (gate), reset by the
+// gated worker once it passes.
+__global__ __launch_bounds__(64) void sched_probe_kernel(int32_t num_tiles, int32_t num_workers, int32_t mode,
+                                                         int32_t gate_worker, int64_t work_ticks,
+                                                         int64_t spin_limit, int32_t *out_tiles,
+                                                         int32_t *out_counts, int32_t max_per_worker,
+                                                         uint32_t *counters, uint32_t *status)
+{
+    __shared__ int32_t slots[2];
+    const bool leader = threadIdx.x == 0;
+    const int w = blockIdx.x;
+
+    if (w == gate_worker) {
+        int64_t polls = 0;
+        while (__hip_atomic_load(counters + 4, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <
+                   (uint32_t)(num_workers - 1) &&
+               polls < spin_limit) {
+            __builtin_amdgcn_s_sleep(8);
+            ++polls;
+        }
+        if (polls >= spin_limit && leader)
+            __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (leader)
+            __hip_atomic_store(counters + 4, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    TileScheduler sched{counters, num_tiles, num_workers, w, mode, slots, 0u};
+    int t = sched.first(leader);
+    int seq = 0;
+    while (t < num_tiles) {
+        sched.claim_ahead(leader);
+        if (leader && seq < max_per_worker)
+            out_tiles[(int64_t)w * max_per_worker + seq] = t;
+        const uint64_t t0 = realtime();
+        while ((int64_t)(realtime() - t0) < work_ticks)
+            __builtin_amdgcn_s_sleep(1);
+        sched.publish(leader, seq);
+        barrier_lds();
+        t = sched.next(t, seq);
+        ++seq;
+    }
+    if (leader)
+        out_counts[w] = seq;
+    wait_all();
+    if (leader && gate_worker >= 0 && w != gate_worker)
+        __hip_atomic_fetch_add(counters + 4, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    sched.finish(leader);
+}
+
+} // namespace pts

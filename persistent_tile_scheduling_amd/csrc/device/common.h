@@ -1,0 +1,104 @@
+// Device-side helpers shared by every kernel of the library (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pts {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+#define PTS_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+// s_waitcnt immediate for the gfx9 family: vmcnt[3:0] in bits 3:0, expcnt in
+// bits 6:4, lgkmcnt in bits 11:8, vmcnt[5:4] in bits 15:14. A field at its
+// maximum means "do not wait on this counter".
+constexpr int waitcnt_imm(int vm, int exp, int lgkm)
+{
+    return (vm & 0xF) | ((exp & 0x7) << 4) | ((lgkm & 0xF) << 8) | (((vm >> 4) & 0x3) << 14);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+// Vector-memory loads (including global->LDS loads) complete in issue order,
+// so this waits for all but the N youngest loads.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(N, 7, 15));
+}
+
+// Wait for this wave's outstanding LDS operations (and scalar loads).
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 7, 0));
+}
+
+__device__ __forceinline__ void wait_all()
+{
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0, 0));
+}
+
+// Workgroup barrier. The "memory" clobber keeps the compiler from moving
+// memory accesses across it; the hardware ordering of LDS and vector-memory
+// traffic is the caller's job (explicit waits before the barrier). This is
+// used instead of __syncthreads(), whose fence would also wait for every
+// outstanding global->LDS load and so serialize the load pipeline.
+__device__ __forceinline__ void barrier_raw()
+{
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// LDS-visible barrier: this wave's LDS writes complete, then all waves meet.
+__device__ __forceinline__ void barrier_lds()
+{
+    wait_lgkmcnt0();
+    barrier_raw();
+}
+
+// 100 MHz constant-rate device clock, comparable across compute units.
+__device__ __forceinline__ uint64_t realtime()
+{
+    return __builtin_amdgcn_s_memrealtime();
+}
+
+__device__ __forceinline__ uint32_t hw_id_reg()
+{
+    uint32_t v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(v));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t xcc_id_reg()
+{
+    uint32_t v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+    return v & 0xF;
+}
+
+// Hide a value's origin from the optimizer so that expressions built on it
+// are recomputed where used instead of being hoisted out of the persistent
+// loop (where dozens of hoisted addresses would occupy registers for the whole
+// kernel). "s" keeps it in a scalar register, "v" in a vector register.
+__device__ __forceinline__ uint32_t opaque_s(uint32_t v)
+{
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t opaque_v(uint32_t v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+__device__ __forceinline__ int uniform(int v)
+{
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+} // namespace pts

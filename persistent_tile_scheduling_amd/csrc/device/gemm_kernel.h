@@ -1,0 +1,552 @@
+// Persistent bf16 GEMM kernel for gfx950: D = A * B, fp32 accumulate.
+//
+// Dataflow (CUTLASS Task Scheduling page "Pipeline Groups", section
+// "Overview": the GEMM mainloop is the canonical Merge -- smem_a and smem_b are
+// filled by their loaders, consumed together by the MMA into the
+// accumulator, which the store writes to D):
+//
+//   HBM --(128-bit global->LDS loads)--> LDS ring of STAGES stages (A and B)
+//       --(ds_read_b128 fragments)--> v_mfma_f32_32x32x16_bf16, fp32 in AGPRs
+//       --(masked epilogue, fp32 or bf16 round-to-nearest-even)--> D
+//
+// Workgroup: 4 waves in a 2 x 2 grid; each wave owns a (BM/2) x (BN/2) block
+// of the output tile and, for every k-tile, issues its quarter of the ring
+// stage's loads. Load and compute overlap through the ring: while stage s is
+// consumed, the loads for the k-tile STAGES-1 ahead are in flight. The
+// hand-off of a stage (producer commit -> consumer wait, consumer release ->
+// producer acquire, in the pages' acquire/commit/wait/release terms of the
+// "Introduction" page, section "Core Terms") is: wait for this wave's own
+// loads of the stage (vmcnt), then one workgroup barrier, which also proves
+// every wave has finished reading the stage that the next loads overwrite.
+//
+// Per persistent tile the accumulators restart from zero, the MFMA analogue
+// of resetting scale_d per work tile ("Resources" page, per-work-tile state).
+// The k loop is the schedule's domain loop; with one k-tile it is both the
+// first and the last iteration ("Schedules" page, section "First, Last, and
+// Periodic Iteration").
+//
+// Ragged edges: rows of A beyond M and columns of B beyond N are read from
+// the last valid row/column (values land only in output elements that the
+// epilogue masks off); k beyond K is zeroed in LDS after the last k-tile's
+// loads land, so out-of-range k contributes exactly 0. The epilogue writes
+// only i < M, j < N ("Schedules" page, section "Domains": in-range indices
+// only).
+#pragma once
+
+#include "common.h"
+#include "scheduler.h"
+
+namespace pts {
+
+#ifndef PTS_MAX_GROUPS
+#define PTS_MAX_GROUPS 64
+#endif
+
+// One problem of a (grouped) run; plan-owned device table.
+struct GroupDesc {
+    int32_t m, n, k;
+    int32_t tiles_n;     // ceil(n / BN)
+    int32_t tile_begin;  // index of the problem's first tile in the run's tile space
+    int32_t num_k_tiles; // ceil(k / BK)
+    int32_t pad0, pad1;
+    int64_t lda, ldb, ldd;
+};
+
+struct TileTrace {
+    int32_t tile, worker, seq, group, row0, col0;
+    uint32_t hw_id, xcc_id;
+    uint64_t t_start, t_end;
+};
+static_assert(sizeof(TileTrace) == 48, "trace record layout");
+
+struct WorkerTrace {
+    uint64_t t_start, t_end;
+    int32_t tiles, worker;
+    uint32_t hw_id, xcc_id;
+};
+static_assert(sizeof(WorkerTrace) == 32, "trace record layout");
+
+struct GemmArgs {
+    const GroupDesc *groups;
+    uint32_t *counters;
+    uint8_t *trace; // TileTrace[total_tiles] then WorkerTrace[num_workers], or null
+    int32_t group_count;
+    int32_t total_tiles;
+    int32_t num_workers;
+    int32_t schedule;
+    uint64_t d_vec_ok; // bit g: problem g's D rows allow vector stores
+    const uint16_t *a[PTS_MAX_GROUPS];
+    const uint16_t *b[PTS_MAX_GROUPS];
+    void *d[PTS_MAX_GROUPS];
+};
+
+template <int BM_, int BN_, int BK_, int STAGES_, bool OUT_BF16_>
+struct GemmConfig {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+    static constexpr bool OUT_BF16 = OUT_BF16_;
+    static constexpr int WAVES_M = 2, WAVES_N = 2, WAVES = 4, THREADS = 256;
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N; // wave tile
+    static constexpr int MI = WTM / 32, NI = WTN / 32;           // 32x32 MFMA blocks per wave
+    static constexpr int KSTEPS = BK / 16;                       // MFMA k-steps per k-tile
+    static constexpr int ROW_BYTES = BK * 2;                     // one row of A (column of B) per k-tile
+    static constexpr int CHUNKS = BK / 8;                        // 16-byte chunks per row
+    static constexpr int A_BYTES = BM * ROW_BYTES, B_BYTES = BN * ROW_BYTES;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int ROWS_PER_LOAD = 1024 / ROW_BYTES;       // rows one wave-wide 16 B/lane load covers
+    static constexpr int A_LOADS = A_BYTES / 1024 / WAVES;       // per wave (= per thread) per stage
+    static constexpr int B_LOADS = B_BYTES / 1024 / WAVES;
+    static constexpr int LOADS = A_LOADS + B_LOADS;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+    static_assert(BK == 32 || BK == 64, "k-tile");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+    static_assert(A_LOADS >= 1 && B_LOADS >= 1 && A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0,
+                  "stage must split into whole 1 KiB wave loads");
+    static_assert(STAGES >= 2 && (STAGES - 2) * LOADS <= 63, "vmcnt range");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
+};
+
+// LDS layout of one operand tile in a stage: row r (a row of A or a column of
+// B) holds its BK k-values in CHUNKS 16-byte chunks; logical chunk c sits at
+// physical position c ^ swz(r). The XOR spreads the 16-byte fragment reads of
+// one MFMA operand (16 consecutive rows, one chunk each) over distinct bank
+// groups whether the LDS serves 8 or 16 lanes per cycle. swz depends on
+// r mod 16 only, so a lane's fragment offsets repeat every 16 rows and the
+// per-block differences become instruction immediates.
+template <int BK>
+__device__ __forceinline__ int lds_swizzle(int r)
+{
+    if constexpr (BK == 64)
+        return (r ^ ((r >> 3) & 1)) & 7;
+    else
+        return ((r >> 1) ^ ((r >> 3) & 1)) & 3;
+}
+
+template <class C>
+__device__ __forceinline__ int lds_offset(int r, int c)
+{
+    return r * C::ROW_BYTES + ((c ^ lds_swizzle<C::BK>(r)) << 4);
+}
+
+// Wait until this wave's loads of the oldest in-flight stage have landed,
+// given how many younger stages (each C::LOADS loads) are still in flight.
+// Global->LDS loads complete in issue order, so vmcnt(younger * LOADS) does it.
+template <class C, int N>
+__device__ __forceinline__ void wait_stage_loads(int younger)
+{
+    if constexpr (N <= 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (younger >= N)
+            wait_vmcnt<N * C::LOADS>();
+        else
+            wait_stage_loads<C, N - 1>(younger);
+    }
+}
+
+template <class C>
+struct TileCtx {
+    int group;
+    int row0, col0, vm, vn; // tile origin and valid extent
+    int k, nk;
+    int64_t lda, ldb, ldd;
+    const uint16_t *a;
+    const uint16_t *b;
+    void *d;
+    bool vec_ok;
+};
+
+// The kernel's argument block, read in place through the kernarg segment
+// pointer: indexing its per-problem pointer arrays with a tile-dependent
+// problem index then compiles to scalar loads instead of a private copy.
+typedef const __attribute__((address_space(4))) GemmArgs *KernArgs;
+
+__device__ __forceinline__ KernArgs kernel_args()
+{
+    return (KernArgs)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
+template <class C>
+__device__ __forceinline__ TileCtx<C> decode_tile(KernArgs args, int t)
+{
+    // problem: the last g with tile_begin <= t (offsets are non-decreasing)
+    const GroupDesc *groups = args->groups;
+    int lo = 0, hi = args->group_count - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (groups[mid].tile_begin <= t)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const int g = uniform(lo);
+    const GroupDesc gd = groups[g];
+    const int local = t - gd.tile_begin;
+    const int tm = local / gd.tiles_n, tn = local - tm * gd.tiles_n;
+    TileCtx<C> c;
+    c.group = g;
+    c.row0 = tm * C::BM;
+    c.col0 = tn * C::BN;
+    c.vm = min(C::BM, gd.m - c.row0);
+    c.vn = min(C::BN, gd.n - c.col0);
+    c.k = gd.k;
+    c.nk = gd.num_k_tiles;
+    c.lda = gd.lda;
+    c.ldb = gd.ldb;
+    c.ldd = gd.ldd;
+    c.a = args->a[g];
+    c.b = args->b[g];
+    c.d = args->d[g];
+    c.vec_ok = (args->d_vec_ok >> g) & 1;
+    return c;
+}
+
+// Raw buffer descriptor over `base` (no range clamping in use: the byte
+// offsets this kernel forms always stay inside the operand).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, -1, 0x00020000);
+}
+
+template <class C>
+struct Mainloop {
+    uint8_t *smem;
+    int wave, lane, wm, wn;
+    // Operand tiles as buffer descriptors (scalar registers); each load
+    // address is descriptor + this thread's 32-bit byte offset + the k-tile's
+    // byte offset (a scalar).
+    __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc;
+    uint32_t a_off[C::A_LOADS];
+    uint32_t b_off[C::B_LOADS];
+
+    // logical k-chunk carried by this thread's i-th load (same for A and B)
+    __device__ __forceinline__ int load_chunk(int i, int nloads) const
+    {
+        const int r = (wave * nloads + i) * C::ROWS_PER_LOAD + lane / C::CHUNKS;
+        return (lane % C::CHUNKS) ^ lds_swizzle<C::BK>(r);
+    }
+
+    __device__ __forceinline__ void setup(const TileCtx<C> &t)
+    {
+        a_rsrc = make_rsrc(t.a + (int64_t)t.row0 * t.lda);
+        b_rsrc = make_rsrc(t.b + (int64_t)t.col0 * t.ldb);
+        const int rl = lane / C::CHUNKS;
+#pragma unroll
+        for (int i = 0; i < C::A_LOADS; ++i) {
+            const int r = (wave * C::A_LOADS + i) * C::ROWS_PER_LOAD + rl;
+            a_off[i] = (uint32_t)((int64_t)min(r, t.vm - 1) * t.lda * 2) + load_chunk(i, C::A_LOADS) * 16;
+        }
+#pragma unroll
+        for (int i = 0; i < C::B_LOADS; ++i) {
+            const int r = (wave * C::B_LOADS + i) * C::ROWS_PER_LOAD + rl;
+            b_off[i] = (uint32_t)((int64_t)min(r, t.vn - 1) * t.ldb * 2) + load_chunk(i, C::B_LOADS) * 16;
+        }
+    }
+
+    // Issue this wave's loads of k-tile kt into ring stage `stage`: one
+    // wave-wide 16-byte-per-lane global->LDS load fills 1 KiB of the stage.
+    template <bool TAIL>
+    __device__ __forceinline__ void issue(int kt, int stage, int k)
+    {
+        const uint32_t wbase = opaque_s((uint32_t)(stage * C::STAGE_BYTES + wave * C::A_LOADS * 1024));
+        uint8_t *sa = smem + wbase - wave * C::A_LOADS * 1024;
+        uint8_t *sb = sa + C::A_BYTES;
+        const uint32_t kbytes = (uint32_t)kt * C::BK * 2;
+        // last 16-byte chunk start inside the rows' readable extent
+        const int klast = ((k + 7) & ~7) - 8;
+#pragma unroll
+        for (int i = 0; i < C::A_LOADS; ++i) {
+            uint32_t off = a_off[i], soff = kbytes;
+            if constexpr (TAIL) {
+                const int c = load_chunk(i, C::A_LOADS);
+                off = off - c * 16 + min(kt * C::BK + c * 8, klast) * 2;
+                soff = 0;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, PTS_LDS_PTR(sa + (wave * C::A_LOADS + i) * 1024), 16,
+                                                     off, soff, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < C::B_LOADS; ++i) {
+            uint32_t off = b_off[i], soff = kbytes;
+            if constexpr (TAIL) {
+                const int c = load_chunk(i, C::B_LOADS);
+                off = off - c * 16 + min(kt * C::BK + c * 8, klast) * 2;
+                soff = 0;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, PTS_LDS_PTR(sb + (wave * C::B_LOADS + i) * 1024), 16,
+                                                     off, soff, 0, 0);
+        }
+    }
+
+    __device__ __forceinline__ void issue_any(int kt, int stage, int k, int nk)
+    {
+        if ((k % C::BK) != 0 && kt == nk - 1)
+            issue<true>(kt, stage, k);
+        else
+            issue<false>(kt, stage, k);
+    }
+
+    __device__ __forceinline__ void zero_chunk_tail(uint8_t *slot, int k0, int k)
+    {
+        if (k0 + 8 <= k)
+            return;
+        u16x8 v = *(u16x8 *)slot;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (k0 + e >= k)
+                v[e] = 0;
+        *(u16x8 *)slot = v;
+    }
+
+    // Zero the k >= K part of the chunks this thread loaded into `stage`
+    // (last k-tile only; this thread's loads of the stage have landed).
+    __device__ __forceinline__ void zero_k_tail(int kt, int stage, int k)
+    {
+        uint8_t *sa = smem + stage * C::STAGE_BYTES;
+        uint8_t *sb = sa + C::A_BYTES;
+        const int koff = kt * C::BK;
+#pragma unroll
+        for (int i = 0; i < C::A_LOADS; ++i)
+            zero_chunk_tail(sa + (wave * C::A_LOADS + i) * 1024 + lane * 16, koff + load_chunk(i, C::A_LOADS) * 8, k);
+#pragma unroll
+        for (int i = 0; i < C::B_LOADS; ++i)
+            zero_chunk_tail(sb + (wave * C::B_LOADS + i) * 1024 + lane * 16, koff + load_chunk(i, C::B_LOADS) * 8, k);
+    }
+
+    // Byte offset, inside a 32-row block, of this lane's fragment for k-step
+    // ks: row lane%32, logical chunk 2*ks + lane/32.
+    uint32_t frag_off[C::KSTEPS];
+
+    __device__ __forceinline__ void setup_fragments()
+    {
+        const int lr = lane & 31, lk = lane >> 5;
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks)
+            frag_off[ks] = (uint32_t)(lr * C::ROW_BYTES + (((2 * ks + lk) ^ lds_swizzle<C::BK>(lr)) << 4));
+    }
+
+    __device__ __forceinline__ void compute(int stage, f32x16 (&acc)[C::MI][C::NI])
+    {
+        const uint32_t sbase = opaque_s((uint32_t)(stage * C::STAGE_BYTES));
+        const uint8_t *sa = smem + sbase + wm * C::WTM * C::ROW_BYTES;
+        const uint8_t *sb = smem + sbase + C::A_BYTES + wn * C::WTN * C::ROW_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) {
+            bf16x8 af[C::MI], bfr[C::NI];
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+                af[mi] = *(const bf16x8 *)(sa + frag_off[ks] + mi * 32 * C::ROW_BYTES);
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+                bfr[ni] = *(const bf16x8 *)(sb + frag_off[ks] + ni * 32 * C::ROW_BYTES);
+            // B fragment as the MFMA's first operand: the 32x32 result block is
+            // D^T, so each lane ends up holding 4 consecutive columns of one row.
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < C::NI; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+        }
+    }
+
+    __device__ __forceinline__ void run(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI])
+    {
+        const int nk = t.nk;
+        const int pro = min(C::STAGES - 1, nk);
+        for (int s = 0; s < pro; ++s)
+            issue_any(s, s, t.k, nk);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int stage = kt % C::STAGES;
+            // this wave's loads of k-tile kt are complete once at most the
+            // younger stages' loads remain outstanding
+            wait_stage_loads<C, C::STAGES - 2>(min(C::STAGES - 2, nk - 1 - kt));
+            if ((t.k % C::BK) != 0 && kt == nk - 1)
+                zero_k_tail(kt, stage, t.k);
+            barrier_lds();
+            if (kt + C::STAGES - 1 < nk)
+                issue_any(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES, t.k, nk);
+            compute(stage, acc);
+        }
+    }
+};
+
+// Epilogue: accumulators -> LDS -> D.
+//
+// With the B fragment as the MFMA's first operand, lane l of 32x32 block
+// (mi, ni) holds, for q = 0..3, the four consecutive columns 8q + 4(l/32) .. +3
+// of row l%32 in acc[4q .. 4q+3]. Each wave writes those 4-element groups
+// as fp32 into a row-major staging tile in LDS (the ring is idle once the k
+// loop has ended; LDS stores take the accumulator registers directly); then
+// the workgroup stores the tile row by row, 4 elements per lane, converting
+// to bf16 there when D is bf16, so each wave writes whole contiguous row
+// segments of D. Rows are padded by 16 bytes so the 32 rows a wave writes in
+// one instruction fall in distinct LDS banks.
+// Only rows < M and columns < N of the problem are written ("Schedules" page,
+// section "Domains": an index is stored only while it is in range).
+template <class C>
+struct Epilogue {
+    static constexpr int ES = C::OUT_BF16 ? 2 : 4;   // bytes per element of D
+    static constexpr int PITCH = C::BN * 4 + 16;     // staged row, fp32
+    // 256-row tiles are staged in two halves to fit LDS
+    static constexpr int PASSES = (C::BM * PITCH > 150 * 1024) ? 2 : 1;
+    static constexpr int PASS_ROWS = C::BM / PASSES;         // staged rows per pass
+    static constexpr int WAVE_ROWS = C::WTM / PASSES;        // a wave's rows per pass
+    static constexpr int MI_PASS = C::MI / PASSES;
+    static constexpr int CHUNKS_ROW = C::BN / 4;             // 4-element groups per row
+    static constexpr int LDS_BYTES = PASS_ROWS * PITCH;
+    static_assert(C::MI % PASSES == 0, "passes split the wave's row blocks");
+    static_assert(LDS_BYTES <= 150 * 1024, "epilogue staging must fit LDS");
+};
+
+template <class C>
+__device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const f32x16 (&acc)[C::MI][C::NI],
+                                               int wm, int wn, int lane, int tid, uint8_t *smem)
+{
+    using E = Epilogue<C>;
+    const int lr = lane & 31, lc = (lane >> 5) * 4;
+    uint8_t *const tile_base = (uint8_t *)t.d + ((int64_t)t.row0 * t.ldd + t.col0) * E::ES;
+#pragma unroll
+    for (int pass = 0; pass < E::PASSES; ++pass) {
+        // accumulators of this pass's row blocks -> LDS
+#pragma unroll
+        for (int m = 0; m < E::MI_PASS; ++m) {
+            const int mi = pass * E::MI_PASS + m;
+            const int sr = wm * E::WAVE_ROWS + m * 32 + lr;
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = wn * C::WTN + ni * 32 + 8 * q + lc;
+                    *(f32x4 *)(smem + sr * E::PITCH + c * 4) =
+                        f32x4{acc[mi][ni][4 * q + 0], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                              acc[mi][ni][4 * q + 3]};
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        barrier_lds();
+        // LDS -> D, one 4-element group per lane per step
+        constexpr int TOTAL = E::PASS_ROWS * E::CHUNKS_ROW;
+#pragma unroll 2
+        for (int idx = tid; idx < TOTAL; idx += C::THREADS) {
+            const int sr = idx / E::CHUNKS_ROW;
+            const int c = (idx % E::CHUNKS_ROW) * 4;
+            // staged row -> tile row
+            const int i = (sr / E::WAVE_ROWS) * C::WTM + pass * E::WAVE_ROWS + (sr % E::WAVE_ROWS);
+            if (i >= t.vm || c >= t.vn)
+                continue;
+            const f32x4 v32 = *(const f32x4 *)(smem + sr * E::PITCH + c * 4);
+            uint8_t *dst = tile_base + ((int64_t)i * t.ldd + c) * E::ES;
+            if constexpr (C::OUT_BF16) {
+                bf16x4 v;
+                v[0] = (__bf16)v32[0];
+                v[1] = (__bf16)v32[1];
+                v[2] = (__bf16)v32[2];
+                v[3] = (__bf16)v32[3];
+                if (t.vec_ok && c + 3 < t.vn) {
+                    *(bf16x4 *)dst = v;
+                } else {
+                    for (int e = 0; e < 4 && c + e < t.vn; ++e)
+                        ((__bf16 *)dst)[e] = v[e];
+                }
+            } else {
+                const f32x4 v = v32;
+                if (t.vec_ok && c + 3 < t.vn) {
+                    *(f32x4 *)dst = v;
+                } else {
+                    for (int e = 0; e < 4 && c + e < t.vn; ++e)
+                        ((float *)dst)[e] = v[e];
+                }
+            }
+        }
+        if (pass + 1 < E::PASSES)
+            barrier_lds();
+    }
+}
+
+template <class C>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void gemm_persistent_kernel(const GemmArgs args_by_value)
+{
+    (void)args_by_value;
+    const KernArgs args = kernel_args();
+    constexpr int SMEM_BYTES = C::LDS_BYTES > Epilogue<C>::LDS_BYTES ? C::LDS_BYTES : Epilogue<C>::LDS_BYTES;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
+    __shared__ int32_t sched_slots[2];
+
+    const int tid = threadIdx.x;
+    const int wave = uniform(tid >> 6);
+    const int lane = tid & 63;
+    const bool leader = tid == 0;
+
+    Mainloop<C> ml;
+    ml.smem = smem;
+    ml.wave = wave;
+    ml.lane = lane;
+    ml.wm = wave / C::WAVES_N;
+    ml.wn = wave % C::WAVES_N;
+    ml.setup_fragments();
+
+    TileScheduler sched{args->counters, args->total_tiles, args->num_workers, (int)blockIdx.x, args->schedule,
+                        sched_slots, 0u};
+    uint8_t *const trace = args->trace;
+    const int total_tiles = args->total_tiles;
+    const bool tracing = trace != nullptr;
+    const uint64_t t_worker0 = tracing ? realtime() : 0;
+
+    int t = sched.first(leader);
+    int seq = 0;
+    while (t < total_tiles) {
+        const uint64_t t_tile0 = tracing ? realtime() : 0;
+        sched.claim_ahead(leader);
+        const TileCtx<C> tc = decode_tile<C>(args, t);
+
+        f32x16 acc[C::MI][C::NI];
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+                acc[mi][ni] = f32x16{};
+
+        ml.setup(tc);
+        ml.run(tc, acc);
+        // every wave has finished reading the ring before it is reused for staging
+        barrier_raw();
+        store_epilogue<C>(tc, acc, ml.wm, ml.wn, lane, tid, smem);
+
+        if (tracing && leader) {
+            TileTrace r;
+            r.tile = t;
+            r.worker = blockIdx.x;
+            r.seq = seq;
+            r.group = tc.group;
+            r.row0 = tc.row0;
+            r.col0 = tc.col0;
+            r.hw_id = hw_id_reg();
+            r.xcc_id = xcc_id_reg();
+            r.t_start = t_tile0;
+            r.t_end = realtime();
+            ((TileTrace *)trace)[t] = r;
+        }
+        sched.publish(leader, seq);
+        // Stores and loads may retire out of order with respect to each other,
+        // so the next tile's load accounting starts from an empty counter.
+        wait_all();
+        barrier_raw();
+        t = sched.next(t, seq);
+        ++seq;
+    }
+
+    if (tracing && leader) {
+        WorkerTrace r;
+        r.t_start = t_worker0;
+        r.t_end = realtime();
+        r.tiles = seq;
+        r.worker = blockIdx.x;
+        r.hw_id = hw_id_reg();
+        r.xcc_id = xcc_id_reg();
+        ((WorkerTrace *)(trace + (size_t)total_tiles * sizeof(TileTrace)))[blockIdx.x] = r;
+    }
+    sched.finish(leader);
+}
+
+} // namespace pts

@@ -1,0 +1,395 @@
+// Host side of the C ABI declared in include/pts_gemm.h: plan validation,
+// tile-space construction, plan-owned device memory, and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#define PTS_MAX_GROUPS GEMM_MAX_GROUPS
+#include "pts_gemm.h"
+
+#include "device/aux_kernels.h"
+#include "device/gemm_kernel.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gemm_status fail(gemm_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+gemm_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(GEMM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// One compiled kernel configuration.
+struct KernelEntry {
+    int bm, bn, bk, stages;
+    bool out_bf16;
+    const void *fn;
+    int lds_bytes;
+};
+
+template <int BM, int BN, int BK, int S, bool BF16>
+KernelEntry make_entry()
+{
+    using C = pts::GemmConfig<BM, BN, BK, S, BF16>;
+    return KernelEntry{BM, BN, BK, S, BF16, (const void *)&pts::gemm_persistent_kernel<C>, C::LDS_BYTES};
+}
+
+const std::vector<KernelEntry> &kernel_table()
+{
+    static const std::vector<KernelEntry> table = {
+        make_entry<256, 256, 64, 2, true>(),  make_entry<256, 256, 64, 2, false>(),
+        make_entry<128, 128, 64, 2, true>(),  make_entry<128, 128, 64, 2, false>(),
+        make_entry<64, 64, 64, 2, true>(),    make_entry<64, 64, 64, 2, false>(),
+    };
+    return table;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+} // namespace
+
+struct gemm_plan {
+    int device = 0;
+    int32_t group_count = 0;
+    std::vector<gemm_shape> shapes; // ld values resolved
+    int32_t dtype_d = GEMM_DTYPE_F32;
+    int32_t schedule = GEMM_SCHEDULE_STATIC;
+    KernelEntry kernel{};
+    int64_t total_tiles = 0;
+    int32_t workers = 0;
+    pts::GroupDesc *d_groups = nullptr;
+    uint32_t *d_counters = nullptr;
+    void *trace = nullptr;
+    size_t trace_bytes = 0;
+};
+
+extern "C" {
+
+const char *gemm_status_string(gemm_status s)
+{
+    switch (s) {
+    case GEMM_OK: return "success";
+    case GEMM_ERR_INVALID_VALUE: return "invalid value";
+    case GEMM_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GEMM_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case GEMM_ERR_HIP: return "HIP runtime error";
+    case GEMM_ERR_TIMEOUT: return "device-side wait timed out";
+    }
+    return "unknown status";
+}
+
+const char *gemm_last_error(void) { return g_last_error.c_str(); }
+
+gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
+{
+    if (out_plan == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "out_plan is NULL");
+    *out_plan = nullptr;
+    if (desc == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "desc is NULL");
+    if (desc->group_count < 1)
+        return fail(GEMM_ERR_INVALID_VALUE, "group_count must be >= 1 (got %d)", desc->group_count);
+    if (desc->group_count > GEMM_MAX_GROUPS)
+        return fail(GEMM_ERR_UNSUPPORTED, "group_count %d exceeds GEMM_MAX_GROUPS (%d)", desc->group_count,
+                    GEMM_MAX_GROUPS);
+    if (desc->shapes == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "shapes is NULL");
+    if (desc->layout_a != GEMM_ROW_MAJOR || desc->layout_b != GEMM_COL_MAJOR || desc->layout_d != GEMM_ROW_MAJOR)
+        return fail(GEMM_ERR_UNSUPPORTED, "layouts must be A row-major, B column-major, D row-major");
+    if (desc->dtype_a != GEMM_DTYPE_BF16 || desc->dtype_b != GEMM_DTYPE_BF16 || desc->dtype_acc != GEMM_DTYPE_F32)
+        return fail(GEMM_ERR_UNSUPPORTED, "A and B must be bf16 and the accumulator fp32");
+    if (desc->dtype_d != GEMM_DTYPE_F32 && desc->dtype_d != GEMM_DTYPE_BF16)
+        return fail(GEMM_ERR_UNSUPPORTED, "D must be fp32 or bf16");
+    if (desc->schedule != GEMM_SCHEDULE_STATIC && desc->schedule != GEMM_SCHEDULE_DYNAMIC)
+        return fail(GEMM_ERR_INVALID_VALUE, "schedule must be static (0) or dynamic (1)");
+    if (desc->num_workers < 0)
+        return fail(GEMM_ERR_INVALID_VALUE, "num_workers must be >= 0");
+    if (desc->flags != GEMM_FLAG_NONE)
+        return fail(GEMM_ERR_UNSUPPORTED, "unknown flags 0x%x", desc->flags);
+    int tm = desc->tile_m == 0 ? 256 : desc->tile_m;
+    int tn = desc->tile_n == 0 ? 256 : desc->tile_n;
+    const bool out_bf16 = desc->dtype_d == GEMM_DTYPE_BF16;
+    const KernelEntry *entry = nullptr;
+    for (const KernelEntry &e : kernel_table())
+        if (e.bm == tm && e.bn == tn && e.out_bf16 == out_bf16) {
+            entry = &e;
+            break;
+        }
+    if (entry == nullptr)
+        return fail(GEMM_ERR_UNSUPPORTED, "tile %dx%d is not built (256x256, 128x128, 64x64)", tm, tn);
+
+    auto plan = new (std::nothrow) gemm_plan();
+    if (plan == nullptr)
+        return fail(GEMM_ERR_OUT_OF_MEMORY, "host allocation failed");
+    std::vector<pts::GroupDesc> groups(desc->group_count);
+    int64_t tiles = 0;
+    for (int g = 0; g < desc->group_count; ++g) {
+        gemm_shape s = desc->shapes[g];
+        if (s.m < 0 || s.n < 0 || s.k < 0 || s.m > INT32_MAX || s.n > INT32_MAX || s.k > INT32_MAX) {
+            delete plan;
+            return fail(GEMM_ERR_INVALID_VALUE, "problem %d: m, n, k must be in [0, 2^31)", g);
+        }
+        if (s.lda == 0) s.lda = s.k;
+        if (s.ldb == 0) s.ldb = s.k;
+        if (s.ldd == 0) s.ldd = s.n;
+        if (s.lda < s.k || s.ldb < s.k || s.ldd < s.n || s.lda < 0 || s.ldb < 0 || s.ldd < 0) {
+            delete plan;
+            return fail(GEMM_ERR_INVALID_VALUE, "problem %d: leading dimension smaller than the packed extent", g);
+        }
+        if ((s.lda % 8) != 0 || (s.ldb % 8) != 0) {
+            delete plan;
+            return fail(GEMM_ERR_INVALID_VALUE,
+                        "problem %d: lda (%lld) and ldb (%lld) must be multiples of 8 elements (16-byte rows)", g,
+                        (long long)s.lda, (long long)s.ldb);
+        }
+        // load offsets inside one tile are 32-bit byte offsets from the tile's origin
+        if ((int64_t)(tm - 1) * s.lda * 2 + (s.k + 8) * 2 >= ((int64_t)1 << 31) ||
+            (int64_t)(tn - 1) * s.ldb * 2 + (s.k + 8) * 2 >= ((int64_t)1 << 31)) {
+            delete plan;
+            return fail(GEMM_ERR_UNSUPPORTED, "problem %d: lda/ldb too large for 32-bit tile offsets", g);
+        }
+        plan->shapes.push_back(s);
+        pts::GroupDesc &gd = groups[g];
+        gd.m = (int32_t)s.m;
+        gd.n = (int32_t)s.n;
+        gd.k = (int32_t)s.k;
+        gd.tiles_n = (int32_t)ceil_div(s.n, tn);
+        gd.tile_begin = (int32_t)tiles;
+        gd.num_k_tiles = (int32_t)ceil_div(s.k, entry->bk);
+        gd.pad0 = gd.pad1 = 0;
+        gd.lda = s.lda;
+        gd.ldb = s.ldb;
+        gd.ldd = s.ldd;
+        if (s.m > 0 && s.n > 0)
+            tiles += ceil_div(s.m, tm) * ceil_div(s.n, tn);
+        if (tiles > INT32_MAX / 2) {
+            delete plan;
+            return fail(GEMM_ERR_UNSUPPORTED, "more than 2^30 output tiles");
+        }
+    }
+
+    hipError_t e = hipGetDevice(&plan->device);
+    if (e != hipSuccess) {
+        delete plan;
+        return hip_fail(e, "hipGetDevice");
+    }
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, plan->device);
+    if (e != hipSuccess) {
+        delete plan;
+        return hip_fail(e, "hipDeviceGetAttribute");
+    }
+    int occ = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, entry->fn, 256, 0);
+    if (e != hipSuccess || occ < 1) {
+        delete plan;
+        return e != hipSuccess ? hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor")
+                               : fail(GEMM_ERR_UNSUPPORTED, "kernel cannot be resident on this device");
+    }
+    int64_t workers = desc->num_workers > 0 ? desc->num_workers : std::min<int64_t>(tiles, (int64_t)cus * occ);
+    if (tiles == 0)
+        workers = 0;
+    if (workers > 65535 * 16) {
+        delete plan;
+        return fail(GEMM_ERR_INVALID_VALUE, "num_workers too large");
+    }
+
+    plan->group_count = desc->group_count;
+    plan->dtype_d = desc->dtype_d;
+    plan->schedule = desc->schedule;
+    plan->kernel = *entry;
+    plan->total_tiles = tiles;
+    plan->workers = (int32_t)workers;
+
+    const size_t gbytes = sizeof(pts::GroupDesc) * groups.size();
+    void *mem = nullptr;
+    e = hipMalloc(&mem, gbytes + 128);
+    if (e != hipSuccess) {
+        delete plan;
+        (void)hipGetLastError();
+        return fail(GEMM_ERR_OUT_OF_MEMORY, "hipMalloc of %zu bytes failed", gbytes + 128);
+    }
+    plan->d_groups = (pts::GroupDesc *)mem;
+    plan->d_counters = (uint32_t *)((uint8_t *)mem + gbytes);
+    e = hipMemcpy(plan->d_groups, groups.data(), gbytes, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemset(plan->d_counters, 0, 128);
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipFree(mem);
+        delete plan;
+        return hip_fail(e, "plan upload");
+    }
+    *out_plan = plan;
+    return GEMM_OK;
+}
+
+gemm_status gemm_plan_destroy(gemm_plan *plan)
+{
+    if (plan == nullptr)
+        return GEMM_OK;
+    hipError_t e = hipSuccess;
+    if (plan->d_groups != nullptr)
+        e = hipFree(plan->d_groups);
+    delete plan;
+    return e == hipSuccess ? GEMM_OK : hip_fail(e, "hipFree");
+}
+
+gemm_status gemm_plan_query(const gemm_plan *plan, int64_t *num_tiles, int32_t *num_workers, int32_t *lds_bytes)
+{
+    if (plan == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "plan is NULL");
+    if (num_tiles) *num_tiles = plan->total_tiles;
+    if (num_workers) *num_workers = plan->workers;
+    if (lds_bytes) *lds_bytes = plan->kernel.lds_bytes + 8;
+    return GEMM_OK;
+}
+
+gemm_status gemm_plan_set_trace(gemm_plan *plan, void *device_buf, size_t bytes)
+{
+    if (plan == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "plan is NULL");
+    if (device_buf == nullptr) {
+        plan->trace = nullptr;
+        plan->trace_bytes = 0;
+        return GEMM_OK;
+    }
+    const size_t need = sizeof(pts::TileTrace) * (size_t)plan->total_tiles + sizeof(pts::WorkerTrace) * plan->workers;
+    if (bytes < need)
+        return fail(GEMM_ERR_INVALID_VALUE, "trace buffer of %zu bytes; %zu needed", bytes, need);
+    if (((uintptr_t)device_buf % 16) != 0)
+        return fail(GEMM_ERR_INVALID_VALUE, "trace buffer must be 16-byte aligned");
+    plan->trace = device_buf;
+    plan->trace_bytes = bytes;
+    return GEMM_OK;
+}
+
+gemm_status gemm_plan_read_counters(const gemm_plan *plan, uint32_t out[4])
+{
+    if (plan == nullptr || out == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "plan or out is NULL");
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess)
+        e = hipMemcpy(out, plan->d_counters, 4 * sizeof(uint32_t), hipMemcpyDeviceToHost);
+    return e == hipSuccess ? GEMM_OK : hip_fail(e, "reading counters");
+}
+
+gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream)
+{
+    if (plan == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "plan is NULL");
+    if (ops == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "ops is NULL");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev != plan->device)
+        return fail(GEMM_ERR_INVALID_VALUE, "plan was created on device %d, current device is %d", plan->device, dev);
+
+    pts::GemmArgs args;
+    memset(&args, 0, sizeof args);
+    const size_t esize_d = plan->dtype_d == GEMM_DTYPE_BF16 ? 2 : 4;
+    for (int g = 0; g < plan->group_count; ++g) {
+        const gemm_shape &s = plan->shapes[g];
+        const gemm_operands &o = ops[g];
+        const bool has_tiles = s.m > 0 && s.n > 0;
+        if (has_tiles) {
+            if (o.d == nullptr || (s.k > 0 && (o.a == nullptr || o.b == nullptr)))
+                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: NULL operand pointer", g);
+            if (s.k > 0 && (((uintptr_t)o.a % 16) != 0 || ((uintptr_t)o.b % 16) != 0))
+                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: A and B must be 16-byte aligned", g);
+            if (((uintptr_t)o.d % esize_d) != 0)
+                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: D must be element aligned", g);
+        }
+        args.a[g] = (const uint16_t *)o.a;
+        args.b[g] = (const uint16_t *)o.b;
+        args.d[g] = o.d;
+        const size_t vec_bytes = 4 * esize_d;
+        if (((uintptr_t)o.d % vec_bytes) == 0 && ((size_t)s.ldd * esize_d) % vec_bytes == 0)
+            args.d_vec_ok |= (uint64_t)1 << g;
+    }
+    if (plan->workers == 0)
+        return GEMM_OK;
+    args.groups = plan->d_groups;
+    args.counters = plan->d_counters;
+    args.trace = (uint8_t *)plan->trace;
+    args.group_count = plan->group_count;
+    args.total_tiles = (int32_t)plan->total_tiles;
+    args.num_workers = plan->workers;
+    args.schedule = plan->schedule;
+
+    void *kargs[] = {&args};
+    e = hipLaunchKernel(plan->kernel.fn, dim3(plan->workers), dim3(256), kargs, 0, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipLaunchKernel");
+    return GEMM_OK;
+}
+
+gemm_status pts_copy_int16(const void *src, void *dst, int64_t n, int32_t num_blocks, void *stream)
+{
+    if (n < 0)
+        return fail(GEMM_ERR_INVALID_VALUE, "n must be >= 0");
+    if (n == 0)
+        return GEMM_OK;
+    if (src == nullptr || dst == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "NULL pointer");
+    if (((uintptr_t)src % 16) != 0 || ((uintptr_t)dst % 16) != 0)
+        return fail(GEMM_ERR_INVALID_VALUE, "src and dst must be 16-byte aligned");
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst, bytes = (uintptr_t)n * 2;
+    if (s0 < d0 + bytes && d0 < s0 + bytes)
+        return fail(GEMM_ERR_INVALID_VALUE, "src and dst overlap");
+    int blocks = num_blocks;
+    if (blocks <= 0) {
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess)
+            return hip_fail(e, "device query");
+        blocks = cus * 4;
+    }
+    const int64_t nvec = n / 8;
+    hipLaunchKernelGGL(pts::copy_int16_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const int4 *)src, (int4 *)dst, nvec, (const int16_t *)src, (int16_t *)dst, n);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? GEMM_OK : hip_fail(e, "copy launch");
+}
+
+gemm_status pts_sched_probe(int32_t num_tiles, int32_t num_workers, int32_t schedule, int32_t gate_worker,
+                            int64_t work_ns, int64_t spin_limit, int32_t *out_tiles, int32_t *out_counts,
+                            int32_t max_per_worker, uint32_t *counters, uint32_t *out_status, void *stream)
+{
+    if (num_tiles < 0 || num_workers < 1 || num_workers > 4096 || max_per_worker < 1)
+        return fail(GEMM_ERR_INVALID_VALUE, "bad probe sizes");
+    if (schedule != GEMM_SCHEDULE_STATIC && schedule != GEMM_SCHEDULE_DYNAMIC)
+        return fail(GEMM_ERR_INVALID_VALUE, "bad schedule");
+    if (gate_worker >= num_workers || work_ns < 0 || spin_limit < 0 || work_ns > 1000000000LL)
+        return fail(GEMM_ERR_INVALID_VALUE, "bad probe parameters");
+    if (out_tiles == nullptr || out_counts == nullptr || counters == nullptr || out_status == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "NULL pointer");
+    hipLaunchKernelGGL(pts::sched_probe_kernel, dim3(num_workers), dim3(64), 0, (hipStream_t)stream, num_tiles,
+                       num_workers, schedule, gate_worker, work_ns / 10, spin_limit, out_tiles, out_counts,
+                       max_per_worker, counters, out_status);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? GEMM_OK : hip_fail(e, "probe launch");
+}
+
+} // extern "C"

@@ -1,0 +1,307 @@
+"""GPU parity: the HIP GEMM against the oracle on the same seeded inputs.
+
+Bars (the tolerance is written here, per case):
+* integer-valued inputs -- bit-exact: fp32 output equals the oracle's exact
+  sum, bf16 output equals the oracle's round-to-nearest-even of it;
+* uniform[-1, 1] inputs -- max |D - ref| <= 2e-3 sqrt(K) (fp32 output) or
+  1e-2 sqrt(K) (bf16 output), over every element at oracle-sized shapes and
+  over sampled entries (every tile's four corners plus random entries) at the
+  full configuration sizes;
+* static and dynamic schedules -- bitwise identical D (same tile body).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pts_inputs as gen
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+BOTH = ("static", "dynamic")
+
+
+@pytest.fixture(scope="module")
+def pts():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import persistent_tile_scheduling_amd as mod
+    return mod
+
+
+def _operands(m, n, k, seed, kind="uniform", lda=0, ldb=0):
+    a_bits = gen.operand_a(m, k, seed, lda=lda or None, kind=kind) if m else np.zeros((0, max(lda, k, 8)), np.uint16)
+    b_bits = gen.operand_b(k, n, seed, ldb=ldb or None, kind=kind) if n else np.zeros((0, max(ldb, k, 8)), np.uint16)
+    return a_bits, b_bits
+
+
+def _padded_ld(k):
+    return max(8, (k + 7) // 8 * 8)
+
+
+# ---------------------------------------------------------------------------
+# Config 1: 256^3, fp32 output, 64x64 tiles (16 tiles) -- full oracle
+# ---------------------------------------------------------------------------
+
+def test_config1_256_cube_fp32_64x64(pts):
+    m = n = k = 256
+    a_bits, b_bits = _operands(m, n, k, 0)
+    ref = oracle.gemm(a_bits, b_bits, m, n, k)
+    a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
+    outs = {}
+    for sched in BOTH:
+        U.log(f"config1 256^3 fp32 tile 64x64 schedule={sched}")
+        d, counters, (tiles, workers) = U.run_single(m, n, k, a, b, torch.float32, sched, tile=(64, 64))
+        assert (tiles, workers) == (16, 16)
+        err = U.check_close(d, ref, k, f"config1 {sched}")
+        U.log(f"  max err {err:.3g} (tol {U.tol_for(torch.float32, k):.3g})")
+        outs[sched] = d
+    assert torch.equal(outs["static"], outs["dynamic"])
+
+
+# ---------------------------------------------------------------------------
+# Integer-exact sweep over edge sizes, every tile size, both output types
+# ---------------------------------------------------------------------------
+
+SWEEP = [(1, 1, 1), (7, 7, 7), (63, 65, 64), (64, 64, 64), (65, 63, 65), (127, 129, 128), (128, 128, 127),
+         (129, 127, 129), (255, 257, 256), (256, 256, 255), (257, 255, 257), (1000, 1000, 1000),
+         (1, 1000, 63), (1000, 1, 129), (257, 1, 1), (1, 257, 257), (300, 200, 8), (33, 520, 1000)]
+
+
+@pytest.mark.parametrize("tile", [(64, 64), (128, 128), (256, 256)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_integer_exact_sweep(pts, tile, out_dtype):
+    for (m, n, k) in SWEEP:
+        lda = ldb = _padded_ld(k)
+        a_bits, b_bits = _operands(m, n, k, 3, kind="integer", lda=lda, ldb=ldb)
+        ref = oracle.gemm(a_bits, b_bits, m, n, k, lda=lda, ldb=ldb)
+        a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
+        for sched in BOTH:
+            U.log(f"integer sweep {(m, n, k)} tile {tile} {out_dtype} {sched}")
+            d, _, _ = U.run_single(m, n, k, a, b, out_dtype, sched, tile=tile, lda=lda, ldb=ldb)
+            U.check_exact(d[:m, :n], ref, f"{(m, n, k)} tile {tile} {sched}")
+
+
+# ---------------------------------------------------------------------------
+# Random inputs, ragged medium shapes, full oracle; D padding untouched
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(600, 700, 300), (257, 129, 1000), (1000, 1000, 64), (513, 257, 2000),
+                                   (40, 3000, 100)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_random_ragged_full_oracle(pts, shape, out_dtype):
+    m, n, k = shape
+    lda, ldb, ldd = _padded_ld(k) + 16, _padded_ld(k) + 8, n + 5
+    a_bits, b_bits = _operands(m, n, k, 5, lda=lda, ldb=ldb)
+    ref = oracle.gemm(a_bits, b_bits, m, n, k, lda=lda, ldb=ldb)
+    a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
+    outs = {}
+    for sched in BOTH:
+        U.log(f"ragged {shape} {out_dtype} {sched}")
+        d = torch.full((m + 3, ldd), 7.0, dtype=out_dtype, device=U.DEV)
+        U.run_single(m, n, k, a, b, out_dtype, sched, lda=lda, ldb=ldb, ldd=ldd, d=d)
+        U.check_close(d[:m, :n], ref, k, f"{shape} {sched}")
+        assert torch.all(d[:m, n:] == 7.0), "row padding of D was written"
+        assert torch.all(d[m:] == 7.0), "rows past M were written"
+        outs[sched] = d
+    assert torch.equal(outs["static"], outs["dynamic"])
+
+
+def test_identity_reproduces_a(pts):
+    m, k = 300, 256
+    a_bits = gen.operand_a(m, k, 8)
+    b_bits = np.zeros((k, k), np.uint16)
+    np.fill_diagonal(b_bits, 0x3F80)
+    a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
+    for sched in BOTH:
+        d, _, _ = U.run_single(m, k, k, a, b, torch.bfloat16, sched)
+        assert np.array_equal(U.device_to_bits(d), a_bits), "A . I != A (bf16 output)"
+
+
+def test_ones_closed_form_rne(pts):
+    # K = 3000 and 3016 are ties in bf16; ties-to-even gives 3008 for both.
+    for k, want in ((3000, 3008.0), (3016, 3008.0), (3001, 3008.0), (64, 64.0)):
+        ld = _padded_ld(k)
+        a = torch.zeros((70, ld), dtype=torch.bfloat16, device=U.DEV)
+        a[:, :k] = 1
+        b = torch.zeros((90, ld), dtype=torch.bfloat16, device=U.DEV)
+        b[:, :k] = 1
+        d, _, _ = U.run_single(70, 90, k, a, b, torch.bfloat16, "dynamic", lda=ld, ldb=ld)
+        assert torch.all(d.float() == want), f"K={k}"
+        d32, _, _ = U.run_single(70, 90, k, a, b, torch.float32, "static", lda=ld, ldb=ld)
+        assert torch.all(d32 == float(k))
+
+
+# ---------------------------------------------------------------------------
+# Degenerate shapes
+# ---------------------------------------------------------------------------
+
+def test_k_zero_writes_zeros(pts):
+    for sched in BOTH:
+        d, _, (tiles, _) = U.run_single(300, 200, 0, None, None, torch.float32, sched)
+        assert tiles == 2
+        assert torch.all(d == 0)
+
+
+def test_m_or_n_zero_is_a_noop(pts):
+    for (m, n) in ((0, 100), (100, 0)):
+        d = torch.full((max(m, 1), max(n, 1)), 5.0, device=U.DEV)
+        a = torch.zeros((max(m, 1), 64), dtype=torch.bfloat16, device=U.DEV)
+        b = torch.zeros((max(n, 1), 64), dtype=torch.bfloat16, device=U.DEV)
+        _, _, (tiles, workers) = U.run_single(m, n, 64, a, b, torch.float32, "dynamic", d=d)
+        assert tiles == 0 and workers == 0
+        assert torch.all(d == 5.0)
+
+
+def test_tile_reuse_does_not_accumulate_across_tiles(pts):
+    # one worker runs every tile: each tile's accumulators must restart at zero
+    m, n, k = 512, 512, 128
+    a_bits, b_bits = _operands(m, n, k, 13, kind="integer")
+    ref = oracle.gemm(a_bits, b_bits, m, n, k)
+    a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
+    for sched in BOTH:
+        d, _, (tiles, workers) = U.run_single(m, n, k, a, b, torch.float32, sched, tile=(128, 128), num_workers=1)
+        assert (tiles, workers) == (16, 1)
+        U.check_exact(d, ref, f"single worker {sched}")
+
+
+def test_more_workers_than_tiles(pts):
+    m, n, k = 100, 100, 64
+    a_bits, b_bits = _operands(m, n, k, 2, kind="integer")
+    ref = oracle.gemm(a_bits, b_bits, m, n, k)
+    a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
+    for sched in BOTH:
+        d, counters, (tiles, workers) = U.run_single(m, n, k, a, b, torch.float32, sched, tile=(64, 64),
+                                                     num_workers=9)
+        assert (tiles, workers) == (4, 9)
+        U.check_exact(d, ref, f"9 workers {sched}")
+
+
+# ---------------------------------------------------------------------------
+# Grouped problems, oracle-sized, full oracle
+# ---------------------------------------------------------------------------
+
+def test_grouped_small_full_oracle(pts):
+    rng = np.random.default_rng(4)
+    shapes = [(int(rng.integers(1, 700)), 300, 200) for _ in range(7)] + [(0, 300, 200), (256, 300, 200)]
+    tensors, refs = [], []
+    for g, (m, n, k) in enumerate(shapes):
+        ta, tb = gen.group_tensor_ids(g)
+        a_bits = gen.operand_a(m, k, 1, tensor_id=ta) if m else np.zeros((1, k), np.uint16)
+        b_bits = gen.operand_b(k, n, 1, tensor_id=tb)
+        refs.append(oracle.gemm(a_bits, b_bits, m, n, k))
+        tensors.append((U.bits_to_device(a_bits), U.bits_to_device(b_bits),
+                        torch.full((max(m, 1), n), float("nan"), dtype=torch.bfloat16, device=U.DEV)))
+    outs = {}
+    for sched in BOTH:
+        U.log(f"grouped small {sched}")
+        for (_, _, d) in tensors:
+            d.fill_(float("nan"))
+        with pts.Plan(shapes, torch.bfloat16, schedule=sched) as p:
+            assert p.num_tiles == sum(-(-m // 256) * 2 for (m, _, _) in shapes)
+            p.run(tensors)
+            torch.cuda.synchronize()
+        for g, ((m, n, k), (_, _, d)) in enumerate(zip(shapes, tensors)):
+            if m:
+                U.check_close(d[:m], refs[g], k, f"group {g} {sched}")
+        outs[sched] = [d.clone() for (_, _, d) in tensors]
+    for x, y in zip(outs["static"], outs["dynamic"]):
+        assert torch.equal(x.nan_to_num(0.0), y.nan_to_num(0.0))
+
+
+# ---------------------------------------------------------------------------
+# Full-size configurations: sampled oracle entries + full fp32 property check
+# ---------------------------------------------------------------------------
+
+def _single_full(pts, m, n, k, out_dtype, seed=0):
+    a = U.device_uniform(m, k, seed, gen.TENSOR_A)
+    b = U.device_uniform(n, k, seed, gen.TENSOR_B)
+    (rows, cols), = U.sample_entries([(m, n)], 256, 256, 2048, seed=seed)
+    ref = U.oracle_sampled(seed, gen.TENSOR_A, gen.TENSOR_B, k, rows, cols)
+    outs = {}
+    for sched in BOTH:
+        U.log(f"full {m}x{n}x{k} {out_dtype} {sched}")
+        d, counters, (tiles, workers) = U.run_single(m, n, k, a, b, out_dtype, sched)
+        err = U.check_sampled(d, rows, cols, ref, k, f"{m}x{n}x{k} {sched}")
+        U.log(f"  sampled max err {err:.3g} (tol {U.tol_for(out_dtype, k):.3g}), tiles {tiles} workers {workers}")
+        if sched == "dynamic":
+            assert counters[:3] == [0, 0, tiles + workers]
+        outs[sched] = d
+    assert torch.equal(outs["static"], outs["dynamic"])
+    U.check_against_fp32_matmul(outs["dynamic"], a, b, k, f"{m}x{n}x{k}")
+
+
+def test_generator_on_device_matches_host(pts):
+    t = gen.uniform_bf16_torch(1 << 20, 0, gen.TENSOR_A, U.DEV)
+    assert np.array_equal(U.device_to_bits(t), gen.uniform_bf16_bits(0, gen.TENSOR_A, 1 << 20))
+
+
+def test_config2_8192_cube_bf16_sampled(pts):
+    _single_full(pts, 8192, 8192, 8192, torch.bfloat16)
+
+
+def test_config3_ragged_5000x7000x3000_fp32_sampled(pts):
+    _single_full(pts, 5000, 7000, 3000, torch.float32)
+
+
+def test_config4_grouped_64_problems_sampled(pts):
+    seed, n, k = 0, 4096, 4096
+    ms = gen.grouped_m_draw(seed)
+    shapes = [(m, n, k) for m in ms]
+    tensors = []
+    for g, m in enumerate(ms):
+        ta, tb = gen.group_tensor_ids(g)
+        tensors.append((U.device_uniform(m, k, seed, ta), U.device_uniform(n, k, seed, tb),
+                        torch.empty((m, n), dtype=torch.bfloat16, device=U.DEV)))
+    samples = U.sample_entries([(m, n) for m in ms], 256, 256, 64, seed=1)
+    refs = []
+    for g, (rows, cols) in enumerate(samples):
+        ta, tb = gen.group_tensor_ids(g)
+        refs.append(U.oracle_sampled(seed, ta, tb, k, rows, cols))
+    outs = {}
+    for sched in BOTH:
+        U.log(f"config4 grouped {sched} sum(M)={sum(ms)}")
+        with pts.Plan(shapes, torch.bfloat16, schedule=sched) as p:
+            p.run(tensors)
+            torch.cuda.synchronize()
+            if sched == "dynamic":
+                assert p.counters()[:3] == [0, 0, p.num_tiles + p.num_workers]
+        worst = 0.0
+        for g, ((rows, cols), ref) in enumerate(zip(samples, refs)):
+            worst = max(worst, U.check_sampled(tensors[g][2], rows, cols, ref, k, f"config4 group {g} {sched}"))
+        U.log(f"  sampled max err {worst:.3g}")
+        outs[sched] = [t[2].clone() for t in tensors]
+    for x, y in zip(outs["static"], outs["dynamic"]):
+        assert torch.equal(x, y)
+
+
+def test_config5_with_concurrent_copy_sampled(pts):
+    m = n = 16384
+    k = 8192
+    seed = 0
+    a = U.device_uniform(m, k, seed, gen.TENSOR_A)
+    b = U.device_uniform(n, k, seed, gen.TENSOR_B)
+    (rows, cols), = U.sample_entries([(m, n)], 256, 256, 2048, seed=2)
+    ref = U.oracle_sampled(seed, gen.TENSOR_A, gen.TENSOR_B, k, rows, cols)
+    ncopy = 1 << 30
+    src = gen.uniform_bf16_torch(ncopy, seed, gen.TENSOR_COPY_SRC, U.DEV).view(torch.int16)
+    dst = torch.zeros(ncopy + 64, dtype=torch.int16, device=U.DEV)
+    copy_stream = torch.cuda.Stream()
+    outs = {}
+    for sched in BOTH:
+        U.log(f"config5 {sched} with concurrent copy")
+        dst.zero_()
+        d = torch.empty((m, n), dtype=torch.bfloat16, device=U.DEV)
+        torch.cuda.synchronize()
+        with pts.Plan([(m, n, k)], torch.bfloat16, schedule=sched) as p:
+            pts.pts_copy_int16(src, dst, ncopy, 0, copy_stream)
+            p.run([(a, b, d)])
+            torch.cuda.synchronize()
+        U.check_sampled(d, rows, cols, ref, k, f"config5 {sched}")
+        assert torch.equal(dst[:ncopy], src), "copy result differs"
+        assert torch.all(dst[ncopy:] == 0), "copy wrote past the end"
+        outs[sched] = d
+    assert torch.equal(outs["static"], outs["dynamic"])

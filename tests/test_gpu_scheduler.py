@@ -1,0 +1,144 @@
+"""GPU tests of the persistent tile scheduler (bit-exact index work).
+
+* The scheduler probe replays the example of "Advanced scheduling: Cluster
+  Launch Control", section "Limits of the static persistent scheduler":
+  12 tiles, 4 workers. Static grid-stride must reproduce the printed table
+  (tests/golden), also when worker 3 starts only after the others finished
+  (the launch tail: it still owns 3, 7, 11). Dynamic claiming must process
+  every tile exactly once and leave nothing for the late worker.
+* The GEMM kernel's own per-tile trace must cover every output tile of the
+  problem exactly once, follow the static assignment in static mode, and end
+  each dynamic run with the claim counter at tiles + workers.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pts():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import persistent_tile_scheduling_amd as mod
+    return mod
+
+
+def _golden(golden_dir):
+    table = {}
+    for line in open(os.path.join(golden_dir, "static_grid_stride_12_tiles_4_workers.txt")):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            w, ts = line.split(":")
+            table[int(w)] = [int(t) for t in ts.split()]
+    return table
+
+
+def _probe(pts, tiles, workers, schedule, gate=-1, work_ns=20000, maxpw=None, counters=None):
+    maxpw = maxpw or max(tiles, 1)
+    out = torch.full((workers, maxpw), -1, dtype=torch.int32, device=U.DEV)
+    counts = torch.full((workers,), -1, dtype=torch.int32, device=U.DEV)
+    if counters is None:
+        counters = torch.zeros(8, dtype=torch.int32, device=U.DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=U.DEV)
+    pts.pts_sched_probe(tiles, workers, schedule, gate, work_ns, 2_000_000, out, counts, maxpw, counters, status)
+    torch.cuda.synchronize()
+    assert status.item() == 0, "gate wait expired"
+    cnt = counts.cpu().tolist()
+    rows = out.cpu().tolist()
+    per_worker = [rows[w][:cnt[w]] for w in range(workers)]
+    return per_worker, counters.cpu().tolist()
+
+
+def test_probe_static_matches_printed_example(pts, golden_dir):
+    per_worker, _ = _probe(pts, 12, 4, pts.GEMM_SCHEDULE_STATIC)
+    assert {w: ts for w, ts in enumerate(per_worker)} == _golden(golden_dir)
+
+
+def test_probe_static_late_worker_keeps_its_tiles(pts, golden_dir):
+    per_worker, _ = _probe(pts, 12, 4, pts.GEMM_SCHEDULE_STATIC, gate=3)
+    assert per_worker[3] == [3, 7, 11]
+    assert {w: ts for w, ts in enumerate(per_worker)} == _golden(golden_dir)
+
+
+def test_probe_dynamic_exactly_once(pts):
+    per_worker, counters = _probe(pts, 12, 4, pts.GEMM_SCHEDULE_DYNAMIC)
+    oracle.check_dynamic_claims(per_worker, 12)
+    # every worker's loop ended on exactly one failed claim: 12 + 4 claims
+    assert counters[:4] == [0, 0, 16, 1]
+
+
+def test_probe_dynamic_late_worker_finds_nothing(pts):
+    per_worker, counters = _probe(pts, 12, 4, pts.GEMM_SCHEDULE_DYNAMIC, gate=3)
+    oracle.check_dynamic_claims(per_worker, 12)
+    assert per_worker[3] == []
+    assert counters[2] == 16
+
+
+def test_probe_dynamic_at_scale_and_repeated(pts):
+    # one counter block across runs: each run must leave it reset for the next
+    shared = torch.zeros(8, dtype=torch.int32, device=U.DEV)
+    for run in range(3):
+        per_worker, counters = _probe(pts, 4096, 256, pts.GEMM_SCHEDULE_DYNAMIC, work_ns=2000, counters=shared)
+        oracle.check_dynamic_claims(per_worker, 4096)
+        assert counters[:4] == [0, 0, 4096 + 256, run + 1]
+
+
+def test_probe_static_at_scale(pts):
+    per_worker, _ = _probe(pts, 1000, 256, pts.GEMM_SCHEDULE_STATIC, work_ns=1000)
+    assert per_worker == oracle.static_assignment(1000, 256)
+
+
+def _traced_run(pts, shapes, schedule, tile=(0, 0), num_workers=0, out_dtype=torch.float32, k=64):
+    tensors = []
+    for (m, n) in shapes:
+        tensors.append((torch.zeros((max(m, 1), k), dtype=torch.bfloat16, device=U.DEV),
+                        torch.zeros((max(n, 1), k), dtype=torch.bfloat16, device=U.DEV),
+                        torch.empty((max(m, 1), max(n, 1)), dtype=out_dtype, device=U.DEV)))
+    with pts.Plan([(m, n, k) for (m, n) in shapes], out_dtype, tile, schedule, num_workers) as p:
+        buf = torch.zeros(p.trace_bytes() // 4 + 4, dtype=torch.int32, device=U.DEV)
+        p.set_trace(buf)
+        p.run(tensors)
+        torch.cuda.synchronize()
+        tiles, workers = pts.decode_trace(buf, p.num_tiles, p.num_workers)
+        return tiles.copy(), workers.copy(), p.num_tiles, p.num_workers, p.counters()
+
+
+@pytest.mark.parametrize("schedule", ["static", "dynamic"])
+@pytest.mark.parametrize("shapes,tile", [([(5000, 7000)], (256, 256)), ([(256, 256)], (64, 64)),
+                                         ([(300, 200), (0, 10), (1000, 64), (1, 1)], (128, 128))])
+def test_gemm_trace_covers_every_tile_once(pts, schedule, shapes, tile):
+    tiles, workers, nt, nw, counters = _traced_run(pts, shapes, schedule, tile)
+    want = sorted((g, r0, c0) for (g, r0, c0, _, _) in oracle.tile_coords(shapes, *tile))
+    got = sorted(zip(tiles["group"].tolist(), tiles["row0"].tolist(), tiles["col0"].tolist()))
+    assert got == want
+    assert sorted(tiles["tile"].tolist()) == list(range(nt))
+    per_worker = [[] for _ in range(nw)]
+    for rec in sorted(tiles.tolist(), key=lambda r: (r[1], r[2])):
+        per_worker[rec[1]].append(rec[0])
+    assert [len(p) for p in per_worker] == workers["tiles"].tolist()
+    assert workers["worker"].tolist() == list(range(nw))
+    assert np.all(tiles["t_end"] >= tiles["t_start"])
+    if schedule == "static":
+        assert per_worker == oracle.static_assignment(nt, nw)
+    else:
+        oracle.check_dynamic_claims(per_worker, nt)
+        assert counters[:3] == [0, 0, nt + nw]
+
+
+def test_copy_kernel(pts):
+    for n in (1, 7, 8, 9, 4096 + 3, (1 << 22) + 5):
+        src = torch.randint(-32768, 32767, (n,), dtype=torch.int16, device=U.DEV)
+        dst = torch.full((n + 40,), 1234, dtype=torch.int16, device=U.DEV)
+        pts.pts_copy_int16(src, dst, n)
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:n], src)
+        assert torch.all(dst[n:] == 1234)
