@@ -95,6 +95,12 @@ typedef struct {
     int32_t dtype_acc;         /* GEMM_DTYPE_F32 */
     int32_t dtype_d;           /* GEMM_DTYPE_F32 or GEMM_DTYPE_BF16 */
     int32_t tile_m, tile_n;    /* output tile; 0 = 256. Built: 256x256, 128x128, 64x64 */
+    int32_t tile_k;            /* k-tile depth of one LDS ring stage: 0 = default, 32 or 64 */
+    int32_t stages;            /* LDS ring stages: 0 = default for tile_k (64: 2, 32: 4) */
+    int32_t load_path;         /* how a ring stage is filled: 0 = default, 1 = global->LDS loads,
+                                  2 = global->registers->LDS (256x256, tile_k 64, 2 stages) */
+    int32_t waves;             /* waves per workgroup: 0 = default, 4 (one per SIMD) or 8 (two per
+                                  SIMD; 256x256, tile_k 64, 2 stages) */
     int32_t schedule;          /* gemm_schedule */
     int32_t num_workers;       /* 0 = one per compute unit times occupancy, capped at the tile count */
     uint32_t flags;            /* GEMM_FLAG_* */

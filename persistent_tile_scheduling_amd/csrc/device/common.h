@@ -11,6 +11,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define PTS_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
@@ -58,6 +59,42 @@ __device__ __forceinline__ void barrier_lds()
 {
     wait_lgkmcnt0();
     barrier_raw();
+}
+
+// Raw buffer descriptor (gfx9 layout) over `base`: no stride, no swizzle,
+// 32-bit data format, and a record count that disables range clamping (the
+// offsets this library forms always stay inside the operand).
+__device__ __forceinline__ u32x4 buffer_rsrc(const void *base)
+{
+    const uint64_t b = (uint64_t)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu);
+    r[2] = 0xFFFFFFFFu;
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// One wave-wide 16-byte-per-lane global -> LDS load: lane l's 16 bytes from
+// buffer offset voff + soff land at LDS byte lds_addr + 16 l.
+//
+// Written as inline assembly on purpose: the compiler tracks its own LDS-DMA
+// builtins as LDS writes that may alias any later LDS read, and then inserts
+// vector-memory waits before the fragment reads of OTHER ring stages, which
+// serializes the prefetch. Here the kernel alone accounts for these loads
+// (explicit vmcnt waits before each stage is read); M0 carries the LDS
+// destination and is used by nothing else in these kernels.
+__device__ __forceinline__ void dma_load16(uint32_t lds_addr, uint32_t voff, u32x4 rsrc, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
 // 100 MHz constant-rate device clock, comparable across compute units.

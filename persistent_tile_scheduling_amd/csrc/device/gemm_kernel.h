@@ -80,11 +80,24 @@ struct GemmArgs {
     void *d[PTS_MAX_GROUPS];
 };
 
-template <int BM_, int BN_, int BK_, int STAGES_, bool OUT_BF16_>
+// LOAD_PATH: how a ring stage is filled.
+enum : int {
+    LOAD_DMA = 0, // global -> LDS loads (buffer_load ... lds), no registers
+    LOAD_REG = 1  // global -> registers one k-tile ahead, then ds_write
+};
+
+// WAVES_M x WAVES_N waves per workgroup, one wave tile each. 2 x 2 gives one
+// wave per SIMD (512 registers each); 2 x 4 gives two waves per SIMD (256
+// registers each), so one wave's LDS and memory waits overlap the other's
+// MFMAs.
+template <int BM_, int BN_, int BK_, int STAGES_, bool OUT_BF16_, int LOAD_PATH_ = LOAD_DMA, int WAVES_M_ = 2,
+          int WAVES_N_ = 2>
 struct GemmConfig {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
     static constexpr bool OUT_BF16 = OUT_BF16_;
-    static constexpr int WAVES_M = 2, WAVES_N = 2, WAVES = 4, THREADS = 256;
+    static constexpr int LOAD_PATH = LOAD_PATH_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
+    static constexpr int WAVES_PER_SIMD = WAVES / 4;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N; // wave tile
     static constexpr int MI = WTM / 32, NI = WTN / 32;           // 32x32 MFMA blocks per wave
     static constexpr int KSTEPS = BK / 16;                       // MFMA k-steps per k-tile
@@ -200,13 +213,6 @@ __device__ __forceinline__ TileCtx<C> decode_tile(KernArgs args, int t)
     return c;
 }
 
-// Raw buffer descriptor over `base` (no range clamping in use: the byte
-// offsets this kernel forms always stay inside the operand).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, -1, 0x00020000);
-}
-
 template <class C>
 struct Mainloop {
     uint8_t *smem;
@@ -214,7 +220,7 @@ struct Mainloop {
     // Operand tiles as buffer descriptors (scalar registers); each load
     // address is descriptor + this thread's 32-bit byte offset + the k-tile's
     // byte offset (a scalar).
-    __amdgpu_buffer_rsrc_t a_rsrc, b_rsrc;
+    u32x4 a_rsrc, b_rsrc;
     uint32_t a_off[C::A_LOADS];
     uint32_t b_off[C::B_LOADS];
 
@@ -227,8 +233,10 @@ struct Mainloop {
 
     __device__ __forceinline__ void setup(const TileCtx<C> &t)
     {
-        a_rsrc = make_rsrc(t.a + (int64_t)t.row0 * t.lda);
-        b_rsrc = make_rsrc(t.b + (int64_t)t.col0 * t.ldb);
+        a_tile = t.a + (int64_t)t.row0 * t.lda;
+        b_tile = t.b + (int64_t)t.col0 * t.ldb;
+        a_rsrc = buffer_rsrc(a_tile);
+        b_rsrc = buffer_rsrc(b_tile);
         const int rl = lane / C::CHUNKS;
 #pragma unroll
         for (int i = 0; i < C::A_LOADS; ++i) {
@@ -242,39 +250,35 @@ struct Mainloop {
         }
     }
 
-    // Issue this wave's loads of k-tile kt into ring stage `stage`: one
-    // wave-wide 16-byte-per-lane global->LDS load fills 1 KiB of the stage.
+    // Issue load number `i` (0 .. LOADS-1; A loads first) of this wave's share
+    // of k-tile kt into ring stage `stage`: one wave-wide 16-byte-per-lane
+    // global->LDS load fills 1 KiB of the stage.
+    template <bool TAIL>
+    __device__ __forceinline__ void issue_one(int i, int kt, int stage, int k)
+    {
+        const bool is_a = i < C::A_LOADS;
+        const int j = is_a ? i : i - C::A_LOADS;
+        const int nl = is_a ? C::A_LOADS : C::B_LOADS;
+        const uint32_t region = is_a ? 0u : (uint32_t)C::A_BYTES;
+        const uint32_t wbase = opaque_s((uint32_t)(stage * C::STAGE_BYTES) + region + (uint32_t)(wave * nl * 1024));
+        uint32_t off = is_a ? a_off[j] : b_off[j];
+        uint32_t soff = (uint32_t)kt * C::BK * 2;
+        if constexpr (TAIL) {
+            // last 16-byte chunk start inside the rows' readable extent
+            const int klast = ((k + 7) & ~7) - 8;
+            const int c = load_chunk(j, nl);
+            off = off - c * 16 + min(kt * C::BK + c * 8, klast) * 2;
+            soff = 0;
+        }
+        dma_load16(lds_address(smem + wbase + j * 1024), off, is_a ? a_rsrc : b_rsrc, soff);
+    }
+
     template <bool TAIL>
     __device__ __forceinline__ void issue(int kt, int stage, int k)
     {
-        const uint32_t wbase = opaque_s((uint32_t)(stage * C::STAGE_BYTES + wave * C::A_LOADS * 1024));
-        uint8_t *sa = smem + wbase - wave * C::A_LOADS * 1024;
-        uint8_t *sb = sa + C::A_BYTES;
-        const uint32_t kbytes = (uint32_t)kt * C::BK * 2;
-        // last 16-byte chunk start inside the rows' readable extent
-        const int klast = ((k + 7) & ~7) - 8;
 #pragma unroll
-        for (int i = 0; i < C::A_LOADS; ++i) {
-            uint32_t off = a_off[i], soff = kbytes;
-            if constexpr (TAIL) {
-                const int c = load_chunk(i, C::A_LOADS);
-                off = off - c * 16 + min(kt * C::BK + c * 8, klast) * 2;
-                soff = 0;
-            }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, PTS_LDS_PTR(sa + (wave * C::A_LOADS + i) * 1024), 16,
-                                                     off, soff, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < C::B_LOADS; ++i) {
-            uint32_t off = b_off[i], soff = kbytes;
-            if constexpr (TAIL) {
-                const int c = load_chunk(i, C::B_LOADS);
-                off = off - c * 16 + min(kt * C::BK + c * 8, klast) * 2;
-                soff = 0;
-            }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, PTS_LDS_PTR(sb + (wave * C::B_LOADS + i) * 1024), 16,
-                                                     off, soff, 0, 0);
-        }
+        for (int i = 0; i < C::LOADS; ++i)
+            issue_one<TAIL>(i, kt, stage, k);
     }
 
     __device__ __forceinline__ void issue_any(int kt, int stage, int k, int nk)
@@ -324,47 +328,341 @@ struct Mainloop {
             frag_off[ks] = (uint32_t)(lr * C::ROW_BYTES + (((2 * ks + lk) ^ lds_swizzle<C::BK>(lr)) << 4));
     }
 
-    __device__ __forceinline__ void compute(int stage, f32x16 (&acc)[C::MI][C::NI])
+    struct Frags {
+        bf16x8 a[C::MI];
+        bf16x8 b[C::NI];
+    };
+
+    // ds_read_b128 of this wave's A and B fragments for k-step ks of `stage`.
+    __device__ __forceinline__ void load_frags(int stage, int ks, Frags &f) const
     {
         const uint32_t sbase = opaque_s((uint32_t)(stage * C::STAGE_BYTES));
         const uint8_t *sa = smem + sbase + wm * C::WTM * C::ROW_BYTES;
         const uint8_t *sb = smem + sbase + C::A_BYTES + wn * C::WTN * C::ROW_BYTES;
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) {
-            bf16x8 af[C::MI], bfr[C::NI];
+        for (int mi = 0; mi < C::MI; ++mi)
+            f.a[mi] = *(const bf16x8 *)(sa + frag_off[ks] + mi * 32 * C::ROW_BYTES);
 #pragma unroll
-            for (int mi = 0; mi < C::MI; ++mi)
-                af[mi] = *(const bf16x8 *)(sa + frag_off[ks] + mi * 32 * C::ROW_BYTES);
+        for (int ni = 0; ni < C::NI; ++ni)
+            f.b[ni] = *(const bf16x8 *)(sb + frag_off[ks] + ni * 32 * C::ROW_BYTES);
+    }
+
+    // MI x NI MFMAs of one k-step. The B fragment is the MFMA's first
+    // operand: the 32x32 result block is D^T, so each lane ends up holding 4
+    // consecutive columns of one row (what the epilogue wants).
+    static __device__ __forceinline__ void mma(const Frags &f, f32x16 (&acc)[C::MI][C::NI])
+    {
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni)
-                bfr[ni] = *(const bf16x8 *)(sb + frag_off[ks] + ni * 32 * C::ROW_BYTES);
-            // B fragment as the MFMA's first operand: the 32x32 result block is
-            // D^T, so each lane ends up holding 4 consecutive columns of one row.
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
+    }
+
+    // The MFMAs of one k-step with loads [first, first + count) of k-tile
+    // dma_kt issued between them, one load after every MFMAS/count MFMAs, so
+    // the load instructions never stall the MFMA stream in one burst.
+    template <int COUNT>
+    __device__ __forceinline__ void mma_with_loads(const Frags &f, f32x16 (&acc)[C::MI][C::NI], bool dma, int first,
+                                                   int dma_kt, int dma_stage, const TileCtx<C> &t)
+    {
+        constexpr int MFMAS = C::MI * C::NI;
+        constexpr int EVERY = MFMAS / COUNT > 0 ? MFMAS / COUNT : 1;
+        const bool tail = (t.k % C::BK) != 0 && dma_kt == t.nk - 1;
 #pragma unroll
-            for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < C::NI; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+        for (int x = 0; x < MFMAS; ++x) {
+            const int mi = x / C::NI, ni = x % C::NI;
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
+            if (x % EVERY == 0 && x / EVERY < COUNT && dma) {
+                const int i = first + x / EVERY;
+                if (tail)
+                    issue_one<true>(i, dma_kt, dma_stage, t.k);
+                else
+                    issue_one<false>(i, dma_kt, dma_stage, t.k);
+            }
         }
+    }
+
+    // Ask the scheduler to interleave the next k-step's fragment reads with
+    // this k-step's MFMAs (one read after each MFMA, the rest of the MFMAs
+    // after), so LDS latency hides behind matrix work.
+    static __device__ __forceinline__ void interleave_reads_with_mfma()
+    {
+        constexpr int READS = C::MI + C::NI, MFMAS = C::MI * C::NI;
+        constexpr int PAIRS = READS < MFMAS ? READS : MFMAS;
+#pragma unroll
+        for (int i = 0; i < PAIRS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+        }
+        if constexpr (MFMAS > PAIRS)
+            __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - PAIRS, 0);
+        if constexpr (READS > PAIRS)
+            __builtin_amdgcn_sched_group_barrier(0x100, READS - PAIRS, 0);
+    }
+
+    // Wait for this wave's loads of k-tile kt, fix its k tail, then meet the
+    // other waves: after this barrier every wave's loads of kt have landed and
+    // every wave has finished reading the stage that k-tile kt + STAGES - 1
+    // will overwrite.
+    __device__ __forceinline__ void stage_ready(int kt, const TileCtx<C> &t)
+    {
+        wait_stage_loads<C, C::STAGES - 2>(min(C::STAGES - 2, t.nk - 1 - kt));
+        if ((t.k % C::BK) != 0 && kt == t.nk - 1)
+            zero_k_tail(kt, kt % C::STAGES, t.k);
+        barrier_lds();
     }
 
     __device__ __forceinline__ void run(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI])
     {
+        if constexpr (C::LOAD_PATH == LOAD_REG)
+            run_regs(t, acc);
+        else if constexpr (C::STAGES >= 3)
+            run_spread(t, acc);
+        else
+            run_burst(t, acc);
+    }
+
+    // ---- register path ----------------------------------------------------
+    // The wave's LOADS 16-byte chunks of one k-tile, held in registers
+    // between their global load and their LDS store.
+    u32x4 staged[C::LOADS];
+
+    const uint16_t *a_tile, *b_tile; // operand tile origins (register path)
+
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const uint16_t *base) const
+    {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, -1, 0x00020000);
+    }
+
+    // Global load number i of k-tile kt into staged[i]. The chunk's k start
+    // is clamped to the last chunk inside the rows' readable extent, which
+    // changes nothing except in the k-tail tile (whose k >= K part is zeroed
+    // in LDS before it is read), so the same branch-free code serves every
+    // k-tile.
+    __device__ __forceinline__ void gload_one(int i, int kt, const TileCtx<C> &t)
+    {
+        const bool is_a = i < C::A_LOADS;
+        const int j = is_a ? i : i - C::A_LOADS;
+        const int nl = is_a ? C::A_LOADS : C::B_LOADS;
+        const int c = load_chunk(j, nl);
+        const int klast = ((t.k + 7) & ~7) - 8;
+        const uint32_t off = (is_a ? a_off[j] : b_off[j]) - c * 16 + min(kt * C::BK + c * 8, klast) * 2;
+        staged[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_of(is_a ? a_tile : b_tile), off, 0, 0);
+    }
+
+    // LDS store of staged[i] into ring stage `stage` (same layout as a
+    // global->LDS load: lane l's chunk at 16 l inside its 1 KiB block).
+    __device__ __forceinline__ void swrite_one(int i, int stage)
+    {
+        const bool is_a = i < C::A_LOADS;
+        const int j = is_a ? i : i - C::A_LOADS;
+        const int nl = is_a ? C::A_LOADS : C::B_LOADS;
+        const uint32_t region = is_a ? 0u : (uint32_t)C::A_BYTES;
+        const uint32_t wbase = opaque_s((uint32_t)(stage * C::STAGE_BYTES) + region + (uint32_t)(wave * nl * 1024));
+        *(u32x4 *)(smem + wbase + j * 1024 + lane * 16) = staged[i];
+    }
+
+    // One k-step's MFMAs with COUNT staged chunks handed on between them:
+    // chunk i is stored from its registers into `stage`, then the same
+    // registers receive chunk i of k-tile `kt` (ordered by the data
+    // dependency), so every chunk spends one whole k-tile in flight.
+    template <int COUNT>
+    __device__ __forceinline__ void mma_with_staging(const Frags &f, f32x16 (&acc)[C::MI][C::NI], int first,
+                                                     int stage, int kt, const TileCtx<C> &t)
+    {
+        constexpr int MFMAS = C::MI * C::NI;
+        constexpr int EVERY = MFMAS / COUNT > 0 ? MFMAS / COUNT : 1;
+#pragma unroll
+        for (int x = 0; x < MFMAS; ++x) {
+            const int mi = x / C::NI, ni = x % C::NI;
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
+            if (x % EVERY == 0 && x / EVERY < COUNT) {
+                const int i = first + x / EVERY;
+                swrite_one(i, stage);
+                gload_one(i, kt, t);
+            }
+        }
+    }
+
+    template <int KS>
+    __device__ __forceinline__ void regs_kstep_ops(const Frags &f, f32x16 (&acc)[C::MI][C::NI], int stage, int kt_load,
+                                                   const TileCtx<C> &t)
+    {
+        // staging happens in the k-steps [FIRST, KSTEPS-2]: all of them before
+        // the barrier that publishes the stage (the last k-step runs after it)
+        constexpr int HALF = C::KSTEPS / 2;
+        constexpr int FIRST = C::KSTEPS - 1 - HALF;
+        constexpr int PER_STEP = C::LOADS / HALF;
+        if constexpr (KS < FIRST || KS == C::KSTEPS - 1)
+            mma(f, acc);
+        else
+            mma_with_staging<PER_STEP>(f, acc, (KS - FIRST) * PER_STEP, stage ^ 1, kt_load, t);
+    }
+
+    template <int KS>
+    __device__ __forceinline__ void regs_steps(Frags (&f)[2], f32x16 (&acc)[C::MI][C::NI], int stage, int kt_load,
+                                               const TileCtx<C> &t)
+    {
+        if constexpr (KS + 1 < C::KSTEPS) {
+            load_frags(stage, KS + 1, f[(KS + 1) & 1]);
+            regs_kstep_ops<KS>(f[KS & 1], acc, stage, kt_load, t);
+            interleave_reads_with_mfma();
+            regs_steps<KS + 1>(f, acc, stage, kt_load, t);
+        }
+    }
+
+    // Two LDS stages and one register stage. During the middle k-steps of
+    // k-tile kt (reading stage kt%2) each staged chunk of k-tile kt+1 (loaded
+    // during the same k-steps of kt-1) is stored into the other stage, which
+    // every wave left at the barrier that ended kt-1, and its registers then
+    // receive the chunk of k-tile kt+2. One barrier per k-tile publishes the
+    // stores. Past the last k-tile the loads re-read k-tile nk-1 and the
+    // stores go to a stage that is not read again, which keeps the loop free
+    // of branches.
+    __device__ __forceinline__ void run_regs(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI])
+    {
+        static_assert(C::STAGES == 2, "register path uses two LDS stages");
+        static_assert(C::KSTEPS >= 3 && C::KSTEPS % 2 == 0 && C::LOADS % (C::KSTEPS / 2) == 0, "staging split");
         const int nk = t.nk;
+        if (nk == 0)
+            return;
+        const bool ktail = (t.k % C::BK) != 0;
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i)
+            gload_one(i, 0, t);
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i)
+            swrite_one(i, 0);
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i)
+            gload_one(i, min(1, nk - 1), t);
+        if (ktail && nk == 1) {
+            wait_lgkmcnt0();
+            zero_k_tail(0, 0, t.k);
+        }
+        barrier_lds();
+        Frags f[2];
+        load_frags(0, 0, f[0]);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int stage = kt & 1;
+            const int kt_load = min(kt + 2, nk - 1);
+            regs_steps<0>(f, acc, stage, kt_load, t);
+            if (kt + 1 < nk) {
+                if (ktail && kt + 1 == nk - 1) {
+                    wait_lgkmcnt0();
+                    zero_k_tail(kt + 1, stage ^ 1, t.k);
+                }
+                barrier_lds();
+                load_frags(stage ^ 1, 0, f[C::KSTEPS & 1]);
+            }
+            regs_kstep_ops<C::KSTEPS - 1>(f[(C::KSTEPS - 1) & 1], acc, stage, kt_load, t);
+        }
+    }
+
+    // ---- global->LDS path -------------------------------------------------
+    // Two stages: the loads of k-tile kt+2 can only start once every wave has
+    // left stage kt, i.e. at the barrier that ends k-tile kt; they are issued
+    // there in one burst.
+    __device__ __forceinline__ void run_burst(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI])
+    {
+        const int nk = t.nk;
+        if (nk == 0)
+            return;
         const int pro = min(C::STAGES - 1, nk);
         for (int s = 0; s < pro; ++s)
             issue_any(s, s, t.k, nk);
+        stage_ready(0, t);
+        if (C::STAGES - 1 < nk)
+            issue_any(C::STAGES - 1, C::STAGES - 1, t.k, nk);
+        Frags f[2];
+        load_frags(0, 0, f[0]);
         for (int kt = 0; kt < nk; ++kt) {
             const int stage = kt % C::STAGES;
-            // this wave's loads of k-tile kt are complete once at most the
-            // younger stages' loads remain outstanding
-            wait_stage_loads<C, C::STAGES - 2>(min(C::STAGES - 2, nk - 1 - kt));
-            if ((t.k % C::BK) != 0 && kt == nk - 1)
-                zero_k_tail(kt, stage, t.k);
-            barrier_lds();
-            if (kt + C::STAGES - 1 < nk)
-                issue_any(kt + C::STAGES - 1, (kt + C::STAGES - 1) % C::STAGES, t.k, nk);
-            compute(stage, acc);
+#pragma unroll
+            for (int ks = 0; ks + 1 < C::KSTEPS; ++ks) {
+                load_frags(stage, ks + 1, f[(ks + 1) & 1]);
+                mma(f[ks & 1], acc);
+                interleave_reads_with_mfma();
+            }
+            if (kt + 1 < nk) {
+                // k-tile kt+1's stage: ready, then its first fragments, while
+                // the last k-step of kt runs from registers.
+                stage_ready(kt + 1, t);
+                if (kt + C::STAGES < nk)
+                    issue_any(kt + C::STAGES, stage, t.k, nk);
+                load_frags((kt + 1) % C::STAGES, 0, f[C::KSTEPS & 1]);
+            }
+            // one MFMA site for the last k-step keeps the accumulators in one
+            // register class across the loop
+            mma(f[(C::KSTEPS - 1) & 1], acc);
+        }
+    }
+
+    // Three or more stages: the stage that k-tile kt used is free from the
+    // barrier that ends kt, and k-tile kt+STAGES goes into it; its loads are
+    // spread over the MFMAs of k-tile kt+1 (LOADS/KSTEPS per k-step), so they
+    // land STAGES-2 k-tiles before they are read.
+    __device__ __forceinline__ void run_spread(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI])
+    {
+        static_assert(C::LOADS % C::KSTEPS == 0, "loads split evenly over k-steps");
+        constexpr int PER_STEP = C::LOADS / C::KSTEPS;
+        const int nk = t.nk;
+        if (nk == 0)
+            return;
+        const int pro = min(C::STAGES, nk);
+        for (int s = 0; s < pro; ++s)
+            issue_any(s, s, t.k, nk);
+        // k-tile 0: its loads were the oldest of the prologue
+        wait_stage_loads<C, C::STAGES - 1>(min(C::STAGES - 1, nk - 1));
+        if ((t.k % C::BK) != 0 && nk == 1)
+            zero_k_tail(0, 0, t.k);
+        barrier_lds();
+        Frags f[2];
+        load_frags(0, 0, f[0]);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int stage = kt % C::STAGES;
+            // loads of k-tile kt + STAGES - 1 into the stage freed by kt - 1
+            const int dma_kt = kt + C::STAGES - 1;
+            const bool dma = kt >= 1 && dma_kt < nk;
+            const int dma_stage = (kt + C::STAGES - 1) % C::STAGES;
+#pragma unroll
+            for (int ks = 0; ks + 1 < C::KSTEPS; ++ks) {
+                load_frags(stage, ks + 1, f[(ks + 1) & 1]);
+                mma_with_loads<PER_STEP>(f[ks & 1], acc, dma, ks * PER_STEP, dma_kt, dma_stage, t);
+                interleave_reads_with_mfma();
+            }
+            if (kt + 1 < nk) {
+                // loads of k-tile kt+1 landed when at most the later issued
+                // k-tiles remain: kt+2 .. min(kt+STAGES-1, nk-1), counting the
+                // slice of kt+STAGES-1 still to come in this k-tile's last step
+                if (dma)
+                    wait_stage_loads_partial<C::STAGES - 3, PER_STEP * (C::KSTEPS - 1)>(
+                        min(C::STAGES - 3, nk - 1 - (kt + 2)));
+                else
+                    wait_stage_loads<C, C::STAGES - 2>(min(C::STAGES - 2, nk - 1 - (kt + 1)));
+                if ((t.k % C::BK) != 0 && kt + 1 == nk - 1)
+                    zero_k_tail(kt + 1, (kt + 1) % C::STAGES, t.k);
+                barrier_lds();
+                load_frags((kt + 1) % C::STAGES, 0, f[C::KSTEPS & 1]);
+            }
+            mma_with_loads<PER_STEP>(f[(C::KSTEPS - 1) & 1], acc, dma, (C::KSTEPS - 1) * PER_STEP, dma_kt, dma_stage,
+                                     t);
+        }
+    }
+
+    // vmcnt for: `full` whole k-tiles of loads plus `extra` loads younger
+    // than the k-tile being waited for.
+    template <int N, int EXTRA>
+    __device__ __forceinline__ void wait_stage_loads_partial(int full)
+    {
+        if constexpr (N <= 0) {
+            wait_vmcnt<EXTRA>();
+        } else {
+            if (full >= N)
+                wait_vmcnt<N * C::LOADS + EXTRA>();
+            else
+                wait_stage_loads_partial<N - 1, EXTRA>(full);
         }
     }
 };
@@ -464,7 +762,8 @@ __device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const f32x16
 }
 
 template <class C>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(C::THREADS, C::THREADS),
+                          amdgpu_waves_per_eu(C::WAVES_PER_SIMD, C::WAVES_PER_SIMD)))
 void gemm_persistent_kernel(const GemmArgs args_by_value)
 {
     (void)args_by_value;

@@ -39,22 +39,36 @@ gemm_status hip_fail(hipError_t e, const char *what)
 struct KernelEntry {
     int bm, bn, bk, stages;
     bool out_bf16;
+    int load_path;
+    int waves;
     const void *fn;
     int lds_bytes;
 };
 
-template <int BM, int BN, int BK, int S, bool BF16>
+template <int BM, int BN, int BK, int S, bool BF16, int LP = pts::LOAD_DMA, int WM = 2, int WN = 2>
 KernelEntry make_entry()
 {
-    using C = pts::GemmConfig<BM, BN, BK, S, BF16>;
-    return KernelEntry{BM, BN, BK, S, BF16, (const void *)&pts::gemm_persistent_kernel<C>, C::LDS_BYTES};
+    using C = pts::GemmConfig<BM, BN, BK, S, BF16, LP, WM, WN>;
+    return KernelEntry{BM, BN, BK, S, BF16, LP, C::WAVES, (const void *)&pts::gemm_persistent_kernel<C>,
+                       C::LDS_BYTES};
 }
 
 const std::vector<KernelEntry> &kernel_table()
 {
     static const std::vector<KernelEntry> table = {
+        // The first entry of a (tile, output type) pair is its default. For
+        // 256x256 that is 8 waves (two per SIMD) with global->LDS loads: the
+        // fastest measured on 8192^3 (one wave per SIMD leaves the LDS reads
+        // latency-bound).
+        make_entry<256, 256, 64, 2, true, pts::LOAD_DMA, 2, 4>(),
+        make_entry<256, 256, 64, 2, false, pts::LOAD_DMA, 2, 4>(),
+        make_entry<256, 256, 64, 2, true, pts::LOAD_REG, 2, 4>(),
+        make_entry<256, 256, 64, 2, false, pts::LOAD_REG, 2, 4>(),
         make_entry<256, 256, 64, 2, true>(),  make_entry<256, 256, 64, 2, false>(),
+        make_entry<256, 256, 32, 4, true>(),  make_entry<256, 256, 32, 4, false>(),
+        make_entry<256, 256, 64, 2, true, pts::LOAD_REG>(), make_entry<256, 256, 64, 2, false, pts::LOAD_REG>(),
         make_entry<128, 128, 64, 2, true>(),  make_entry<128, 128, 64, 2, false>(),
+        make_entry<128, 128, 32, 4, true>(),  make_entry<128, 128, 32, 4, false>(),
         make_entry<64, 64, 64, 2, true>(),    make_entry<64, 64, 64, 2, false>(),
     };
     return table;
@@ -126,13 +140,20 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
     int tn = desc->tile_n == 0 ? 256 : desc->tile_n;
     const bool out_bf16 = desc->dtype_d == GEMM_DTYPE_BF16;
     const KernelEntry *entry = nullptr;
+    if (desc->tile_k < 0 || desc->stages < 0 || desc->load_path < 0 || desc->load_path > 2 ||
+        (desc->waves != 0 && desc->waves != 4 && desc->waves != 8))
+        return fail(GEMM_ERR_INVALID_VALUE, "tile_k and stages must be >= 0, load_path in 0..2, waves 0, 4 or 8");
     for (const KernelEntry &e : kernel_table())
-        if (e.bm == tm && e.bn == tn && e.out_bf16 == out_bf16) {
+        if (e.bm == tm && e.bn == tn && e.out_bf16 == out_bf16 && (desc->tile_k == 0 || e.bk == desc->tile_k) &&
+            (desc->stages == 0 || e.stages == desc->stages) &&
+            (desc->load_path == 0 || e.load_path == desc->load_path - 1) &&
+            (desc->waves == 0 || e.waves == desc->waves)) {
             entry = &e;
             break;
         }
     if (entry == nullptr)
-        return fail(GEMM_ERR_UNSUPPORTED, "tile %dx%d is not built (256x256, 128x128, 64x64)", tm, tn);
+        return fail(GEMM_ERR_UNSUPPORTED, "tile %dx%d (k %d, %d stages, load path %d) is not built", tm, tn,
+                    desc->tile_k, desc->stages, desc->load_path);
 
     auto plan = new (std::nothrow) gemm_plan();
     if (plan == nullptr)
@@ -196,7 +217,7 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
         return hip_fail(e, "hipDeviceGetAttribute");
     }
     int occ = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, entry->fn, 256, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, entry->fn, entry->waves * 64, 0);
     if (e != hipSuccess || occ < 1) {
         delete plan;
         return e != hipSuccess ? hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor")
@@ -337,7 +358,8 @@ gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream)
     args.schedule = plan->schedule;
 
     void *kargs[] = {&args};
-    e = hipLaunchKernel(plan->kernel.fn, dim3(plan->workers), dim3(256), kargs, 0, (hipStream_t)stream);
+    e = hipLaunchKernel(plan->kernel.fn, dim3(plan->workers), dim3(plan->kernel.waves * 64), kargs, 0,
+                        (hipStream_t)stream);
     if (e != hipSuccess)
         return hip_fail(e, "hipLaunchKernel");
     return GEMM_OK;

@@ -71,7 +71,12 @@ SWEEP = [(1, 1, 1), (7, 7, 7), (63, 65, 64), (64, 64, 64), (65, 63, 65), (127, 1
          (1, 1000, 63), (1000, 1, 129), (257, 1, 1), (1, 257, 257), (300, 200, 8), (33, 520, 1000)]
 
 
-@pytest.mark.parametrize("tile", [(64, 64), (128, 128), (256, 256)])
+# every built kernel: (tile_m, tile_n, tile_k, stages)
+KERNELS = [(64, 64, 64, 2, 1, 4), (128, 128, 64, 2, 1, 4), (128, 128, 32, 4, 1, 4), (256, 256, 64, 2, 1, 4),
+           (256, 256, 32, 4, 1, 4), (256, 256, 64, 2, 2, 4), (256, 256, 64, 2, 2, 8), (256, 256, 64, 2, 1, 8)]
+
+
+@pytest.mark.parametrize("tile", KERNELS)
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_integer_exact_sweep(pts, tile, out_dtype):
     for (m, n, k) in SWEEP:
@@ -92,7 +97,9 @@ def test_integer_exact_sweep(pts, tile, out_dtype):
 @pytest.mark.parametrize("shape", [(600, 700, 300), (257, 129, 1000), (1000, 1000, 64), (513, 257, 2000),
                                    (40, 3000, 100)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_random_ragged_full_oracle(pts, shape, out_dtype):
+@pytest.mark.parametrize("tile", [(256, 256, 64, 2, 1, 4), (256, 256, 32, 4, 1, 4), (256, 256, 64, 2, 2, 4),
+                                  (256, 256, 64, 2, 2, 8), (256, 256, 64, 2, 1, 8)])
+def test_random_ragged_full_oracle(pts, shape, out_dtype, tile):
     m, n, k = shape
     lda, ldb, ldd = _padded_ld(k) + 16, _padded_ld(k) + 8, n + 5
     a_bits, b_bits = _operands(m, n, k, 5, lda=lda, ldb=ldb)
@@ -102,7 +109,7 @@ def test_random_ragged_full_oracle(pts, shape, out_dtype):
     for sched in BOTH:
         U.log(f"ragged {shape} {out_dtype} {sched}")
         d = torch.full((m + 3, ldd), 7.0, dtype=out_dtype, device=U.DEV)
-        U.run_single(m, n, k, a, b, out_dtype, sched, lda=lda, ldb=ldb, ldd=ldd, d=d)
+        U.run_single(m, n, k, a, b, out_dtype, sched, tile=tile, lda=lda, ldb=ldb, ldd=ldd, d=d)
         U.check_close(d[:m, :n], ref, k, f"{shape} {sched}")
         assert torch.all(d[:m, n:] == 7.0), "row padding of D was written"
         assert torch.all(d[m:] == 7.0), "rows past M were written"
