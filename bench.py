@@ -3,8 +3,10 @@
 dynamic tile schedule, one GPU.
 
 A step is one gemm_run of the whole workload (one persistent launch) with the
-inputs already resident in HBM. Both schedules are timed; the JSON line's
-`value` is the dynamic schedule's whole-job throughput and the static one is
+inputs already resident in HBM. Every schedule named by --schedules is timed
+(static grid-stride, dynamic single-counter claiming, dynamic per-XCD
+claiming); the JSON line's `value` is the per-XCD dynamic schedule's
+whole-job throughput (else the single-counter one's) and the others are
 reported beside it. Kernel durations come from HIP events recorded on the
 stream the kernel is launched on.
 
@@ -161,7 +163,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--schedules", default="static,dynamic")
+    ap.add_argument("--schedules", default="static,dynamic,dynamic_xcd")
     ap.add_argument("--tile-k", type=int, default=0, help="k-tile depth (0 = library default)")
     ap.add_argument("--stages", type=int, default=0, help="LDS ring stages (0 = library default)")
     ap.add_argument("--load-path", type=int, default=0, help="1 = global->LDS, 2 = via registers (0 = default)")
@@ -214,7 +216,7 @@ def main():
             r.update(tail_idle(pts, wl, ops, sched, copy_bufs))
         results[sched] = r
 
-    head = results.get("dynamic") or next(iter(results.values()))
+    head = results.get("dynamic_xcd") or results.get("dynamic") or next(iter(results.values()))
     line = {
         "metric": METRIC,
         "value": round(head["tflops"], 2),

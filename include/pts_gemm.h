@@ -67,7 +67,11 @@ typedef enum {
 
 typedef enum { GEMM_DTYPE_BF16 = 0, GEMM_DTYPE_F32 = 1 } gemm_dtype;
 typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout;
-typedef enum { GEMM_SCHEDULE_STATIC = 0, GEMM_SCHEDULE_DYNAMIC = 1 } gemm_schedule;
+/* STATIC: grid-stride. DYNAMIC: every tile claimed from one device-wide
+ * counter. DYNAMIC_XCD: one counter per XCD (chiplet) over a contiguous range
+ * of tiles, so the tiles in flight on an XCD share its L2; a worker whose
+ * XCD's range is used up claims from the other ranges in turn. */
+typedef enum { GEMM_SCHEDULE_STATIC = 0, GEMM_SCHEDULE_DYNAMIC = 1, GEMM_SCHEDULE_DYNAMIC_XCD = 2 } gemm_schedule;
 
 /* Largest group count one plan accepts: the per-problem operand pointers of a
  * run travel in the kernel's argument block. */
@@ -159,13 +163,17 @@ gemm_status gemm_plan_query(const gemm_plan *plan, int64_t *num_tiles, int32_t *
  * Per-tile trace (test and benchmark use). After this call every run writes,
  * into `device_buf`, one record per tile followed by one record per worker:
  *
- *   struct { int32 tile, worker, seq, group, row0, col0; uint32 hw_id, xcc_id;
+ *   struct { int32 tile, claim, worker, seq, group, row0, col0; uint32 xcc_id;
  *            uint64 t_start, t_end; }              -- 48 bytes, at index `tile`
  *   struct { uint64 t_start, t_end; int32 tiles, worker; uint32 hw_id, xcc_id; }
  *                                                  -- 32 bytes, at index `worker`
  *
- * Times are the 100 MHz device real-time counter; seq is the tile's position
- * in its worker's sequence; hw_id is the wave's HW_ID register and xcc_id its
+ * `tile` is the tile's position in the plan's tile order (problems in turn;
+ * inside a problem, groups of 8 tile rows walked column by column), `claim`
+ * the scheduler's value that selected it (static: the logical grid-stride
+ * index; dynamic: the counter value; per-XCD: XCD * 2^24 + counter value).
+ * Times are the 100 MHz device real-time counter; seq is the tile's place in
+ * its worker's sequence; hw_id is the wave's HW_ID register and xcc_id its
  * XCC (chiplet) id. `bytes` must be >= 48 * num_tiles + 32 * num_workers.
  * device_buf = NULL switches tracing off.
  */
@@ -174,9 +182,9 @@ gemm_status gemm_plan_set_trace(gemm_plan *plan, void *device_buf, size_t bytes)
 /*
  * Read the plan's scheduler counters (synchronizes the device): out[0] the
  * live claim counter (0 between dynamic runs), out[1] the live exit counter
- * (0 between runs), out[2] the claim counter's final value in the last
- * dynamic run (tiles + workers: every worker's loop ends on exactly one failed
- * claim), out[3] the number of dynamic runs completed.
+ * (0 between runs), out[2] the total number of claims in the last dynamic run
+ * (single counter: tiles + workers, since every worker's loop ends on exactly
+ * one failed claim), out[3] the number of dynamic runs completed.
  */
 gemm_status gemm_plan_read_counters(const gemm_plan *plan, uint32_t out[4]);
 
@@ -196,9 +204,11 @@ gemm_status pts_copy_int16(const void *src, void *dst, int64_t n, int32_t num_bl
  * and out_counts[w] how many; both are device arrays of num_workers rows.
  * gate_worker >= 0 holds that worker back until all others have finished
  * (bounded by spin_limit polls; on expiry out_status[0] = 1), which replays a
- * worker that starts late. counters: device array of 4 uint32 zeroed by the
- * caller before the first call (the dynamic counter resets itself at the end
- * of every call). out_status: device array of 1 uint32.
+ * worker that starts late. out_tiles holds the logical index (static) or
+ * counter value (dynamic) of each tile, or its position (per-XCD claiming).
+ * counters: device array of 16 uint32 zeroed by the caller before the first
+ * call (the claim counters reset themselves at the end of every call).
+ * out_status: device array of 1 uint32.
  */
 gemm_status pts_sched_probe(int32_t num_tiles, int32_t num_workers, int32_t schedule,
                             int32_t gate_worker, int64_t work_ns, int64_t spin_limit,

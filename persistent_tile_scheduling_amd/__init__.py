@@ -31,6 +31,7 @@ GEMM_ROW_MAJOR = 0
 GEMM_COL_MAJOR = 1
 GEMM_SCHEDULE_STATIC = 0
 GEMM_SCHEDULE_DYNAMIC = 1
+GEMM_SCHEDULE_DYNAMIC_XCD = 2
 GEMM_MAX_GROUPS = 64
 GEMM_FLAG_NONE = 0
 
@@ -203,7 +204,8 @@ class Plan:
     def __init__(self, shapes, out_dtype=torch.float32, tile=(0, 0), schedule: str | int = "static",
                  num_workers: int = 0):
         if isinstance(schedule, str):
-            schedule = {"static": GEMM_SCHEDULE_STATIC, "dynamic": GEMM_SCHEDULE_DYNAMIC}[schedule]
+            schedule = {"static": GEMM_SCHEDULE_STATIC, "dynamic": GEMM_SCHEDULE_DYNAMIC,
+                        "dynamic_xcd": GEMM_SCHEDULE_DYNAMIC_XCD}[schedule]
         dtype_d = {torch.float32: GEMM_DTYPE_F32, torch.bfloat16: GEMM_DTYPE_BF16}[out_dtype]
         self.shapes = [tuple(s) for s in shapes]
         self.out_dtype = out_dtype
@@ -246,8 +248,8 @@ def decode_trace(buf: torch.Tensor, num_tiles: int, num_workers: int):
     """Split a trace buffer (any dtype, on any device) into numpy record arrays."""
     import numpy as np
     raw = buf.detach().cpu().contiguous().view(torch.uint8).numpy()
-    tile_dt = np.dtype([("tile", "<i4"), ("worker", "<i4"), ("seq", "<i4"), ("group", "<i4"), ("row0", "<i4"),
-                        ("col0", "<i4"), ("hw_id", "<u4"), ("xcc_id", "<u4"), ("t_start", "<u8"),
+    tile_dt = np.dtype([("tile", "<i4"), ("claim", "<i4"), ("worker", "<i4"), ("seq", "<i4"), ("group", "<i4"),
+                        ("row0", "<i4"), ("col0", "<i4"), ("xcc_id", "<u4"), ("t_start", "<u8"),
                         ("t_end", "<u8")])
     worker_dt = np.dtype([("t_start", "<u8"), ("t_end", "<u8"), ("tiles", "<i4"), ("worker", "<i4"),
                           ("hw_id", "<u4"), ("xcc_id", "<u4")])

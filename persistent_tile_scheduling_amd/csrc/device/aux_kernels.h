@@ -26,28 +26,29 @@ __global__ __launch_bounds__(256) void copy_int16_kernel(const int4 *__restrict_
 // Scheduler probe: the tile scheduler of the GEMM kernel with a fixed busy
 // wait standing in for a tile's work. One wave per worker.
 //
-// out_tiles[w * max_per_worker + i]: i-th tile of worker w; out_counts[w]:
-// how many. gate_worker (if >= 0) first waits until every other worker has
+// out_tiles[w * max_per_worker + i]: i-th tile of worker w (the logical
+// index for static and single-counter claiming, the tile position for
+// per-XCD claiming); out_counts[w]: how many. gate_worker (if >= 0) first waits until every other worker has
 // finished -- the late-starting worker of "Advanced scheduling: Cluster Launch
 // Control", section "Limits of the static persistent scheduler". The wait
 // polls at most spin_limit times; on expiry status[0] = 1 and the worker goes
 // on, so the kernel always ends.
 //
-// counters: [0..3] as in TileScheduler, [4] workers done (gate), reset by the
-// gated worker once it passes.
+// counters: [0, CTR_WORDS) as in TileScheduler, [CTR_WORDS] workers done
+// (gate), reset by the gated worker once it passes.
 __global__ __launch_bounds__(64) void sched_probe_kernel(int32_t num_tiles, int32_t num_workers, int32_t mode,
                                                          int32_t gate_worker, int64_t work_ticks,
                                                          int64_t spin_limit, int32_t *out_tiles,
                                                          int32_t *out_counts, int32_t max_per_worker,
                                                          uint32_t *counters, uint32_t *status)
 {
-    __shared__ int32_t slots[2];
+    __shared__ int32_t slots[4];
     const bool leader = threadIdx.x == 0;
     const int w = blockIdx.x;
 
     if (w == gate_worker) {
         int64_t polls = 0;
-        while (__hip_atomic_load(counters + 4, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <
+        while (__hip_atomic_load(counters + CTR_WORDS, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <
                    (uint32_t)(num_workers - 1) &&
                polls < spin_limit) {
             __builtin_amdgcn_s_sleep(8);
@@ -56,29 +57,28 @@ __global__ __launch_bounds__(64) void sched_probe_kernel(int32_t num_tiles, int3
         if (polls >= spin_limit && leader)
             __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (leader)
-            __hip_atomic_store(counters + 4, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(counters + CTR_WORDS, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    TileScheduler sched{counters, num_tiles, num_workers, w, mode, slots, 0u};
-    int t = sched.first(leader);
+    TileScheduler sched{counters, num_tiles, num_workers, w, mode, slots, (int)(xcc_id_reg() % NUM_XCD), 0u};
+    Claimed cur = sched.first(leader);
     int seq = 0;
-    while (t < num_tiles) {
+    while (cur.pos < num_tiles) {
         sched.claim_ahead(leader);
         if (leader && seq < max_per_worker)
-            out_tiles[(int64_t)w * max_per_worker + seq] = t;
+            out_tiles[(int64_t)w * max_per_worker + seq] = mode == SCHED_DYNAMIC_XCD ? cur.pos : cur.claim;
         const uint64_t t0 = realtime();
         while ((int64_t)(realtime() - t0) < work_ticks)
             __builtin_amdgcn_s_sleep(1);
-        sched.publish(leader, seq);
         barrier_lds();
-        t = sched.next(t, seq);
+        cur = sched.next(cur, leader, seq);
         ++seq;
     }
     if (leader)
         out_counts[w] = seq;
     wait_all();
     if (leader && gate_worker >= 0 && w != gate_worker)
-        __hip_atomic_fetch_add(counters + 4, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(counters + CTR_WORDS, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     sched.finish(leader);
 }
 

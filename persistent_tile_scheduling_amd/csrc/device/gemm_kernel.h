@@ -53,8 +53,8 @@ struct GroupDesc {
 };
 
 struct TileTrace {
-    int32_t tile, worker, seq, group, row0, col0;
-    uint32_t hw_id, xcc_id;
+    int32_t tile, claim, worker, seq, group, row0, col0;
+    uint32_t xcc_id;
     uint64_t t_start, t_end;
 };
 static_assert(sizeof(TileTrace) == 48, "trace record layout");
@@ -178,6 +178,23 @@ __device__ __forceinline__ KernArgs kernel_args()
     return (KernArgs)__builtin_amdgcn_kernarg_segment_ptr();
 }
 
+// Tile order inside one problem: the tile rows are taken in groups of
+// RASTER_ROWS, and each group is walked column by column, so any run of
+// consecutive positions covers a compact block (8 consecutive positions: one
+// column of 8 tiles; 32: 8 x 4 tiles) whose A and B panels are few and shared.
+// This is an order, not a change of work: every tile has exactly one position.
+constexpr int RASTER_ROWS = 8;
+
+__device__ __forceinline__ void raster_tile(int local, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    const int group = local / (RASTER_ROWS * tiles_n);
+    const int first_row = group * RASTER_ROWS;
+    const int rows = min(RASTER_ROWS, tiles_m - first_row);
+    const int within = local - first_row * tiles_n;
+    tm = first_row + within % rows;
+    tn = within / rows;
+}
+
 template <class C>
 __device__ __forceinline__ TileCtx<C> decode_tile(KernArgs args, int t)
 {
@@ -194,7 +211,8 @@ __device__ __forceinline__ TileCtx<C> decode_tile(KernArgs args, int t)
     const int g = uniform(lo);
     const GroupDesc gd = groups[g];
     const int local = t - gd.tile_begin;
-    const int tm = local / gd.tiles_n, tn = local - tm * gd.tiles_n;
+    int tm, tn;
+    raster_tile(local, (gd.m + C::BM - 1) / C::BM, gd.tiles_n, tm, tn);
     TileCtx<C> c;
     c.group = g;
     c.row0 = tm * C::BM;
@@ -770,7 +788,7 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     const KernArgs args = kernel_args();
     constexpr int SMEM_BYTES = C::LDS_BYTES > Epilogue<C>::LDS_BYTES ? C::LDS_BYTES : Epilogue<C>::LDS_BYTES;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
-    __shared__ int32_t sched_slots[2];
+    __shared__ int32_t sched_slots[4];
 
     const int tid = threadIdx.x;
     const int wave = uniform(tid >> 6);
@@ -786,18 +804,18 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     ml.setup_fragments();
 
     TileScheduler sched{args->counters, args->total_tiles, args->num_workers, (int)blockIdx.x, args->schedule,
-                        sched_slots, 0u};
+                        sched_slots, (int)(xcc_id_reg() % NUM_XCD), 0u};
     uint8_t *const trace = args->trace;
     const int total_tiles = args->total_tiles;
     const bool tracing = trace != nullptr;
     const uint64_t t_worker0 = tracing ? realtime() : 0;
 
-    int t = sched.first(leader);
+    Claimed cur = sched.first(leader);
     int seq = 0;
-    while (t < total_tiles) {
+    while (cur.pos < total_tiles) {
         const uint64_t t_tile0 = tracing ? realtime() : 0;
         sched.claim_ahead(leader);
-        const TileCtx<C> tc = decode_tile<C>(args, t);
+        const TileCtx<C> tc = decode_tile<C>(args, cur.pos);
 
         f32x16 acc[C::MI][C::NI];
 #pragma unroll
@@ -814,24 +832,23 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
 
         if (tracing && leader) {
             TileTrace r;
-            r.tile = t;
+            r.tile = cur.pos;
+            r.claim = cur.claim;
             r.worker = blockIdx.x;
             r.seq = seq;
             r.group = tc.group;
             r.row0 = tc.row0;
             r.col0 = tc.col0;
-            r.hw_id = hw_id_reg();
             r.xcc_id = xcc_id_reg();
             r.t_start = t_tile0;
             r.t_end = realtime();
-            ((TileTrace *)trace)[t] = r;
+            ((TileTrace *)trace)[cur.pos] = r;
         }
-        sched.publish(leader, seq);
         // Stores and loads may retire out of order with respect to each other,
         // so the next tile's load accounting starts from an empty counter.
         wait_all();
         barrier_raw();
-        t = sched.next(t, seq);
+        cur = sched.next(cur, leader, seq);
         ++seq;
     }
 

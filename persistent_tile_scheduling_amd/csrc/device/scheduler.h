@@ -35,78 +35,166 @@
 // Each worker ends on exactly one failed claim, so a run takes T + P claims.
 // The counter resets itself: each worker, after its failed claim, increments
 // an exit counter, and the worker that brings it to P (all claims are done)
-// records the final claim value, zeroes both counters and counts the run.
+// records the final claim total, zeroes the counters and counts the run.
 // A run therefore needs no host-side reset and no memset node.
+//
+// MI355X-specific variant (per-XCD claiming): the eight XCDs have separate
+// L2 caches, and one shared counter hands consecutive tiles to workers on
+// different XCDs, so no L2 sees its neighbours' A and B panels. Instead each
+// XCD owns a counter over a contiguous range of tile positions; a worker
+// claims from its own XCD's range and, once that is used up, from the other
+// ranges in turn (work stealing across XCDs); its loop ends only when every
+// range is used up. Every position is still handed out exactly once.
 #pragma once
 
 #include "common.h"
 
 namespace pts {
 
-enum : int { SCHED_STATIC = 0, SCHED_DYNAMIC = 1 };
+enum : int { SCHED_STATIC = 0, SCHED_DYNAMIC = 1, SCHED_DYNAMIC_XCD = 2 };
 
-// counters[0] claim counter, [1] exit counter, [2] final claim value of the
-// last dynamic run, [3] dynamic runs completed.
+constexpr int NUM_XCD = 8;           // chiplets (XCDs) of an MI355X, each with its own L2
+constexpr int CTR_CLAIM = 0;         // single device-wide claim counter
+constexpr int CTR_EXIT = 1;          // workers that have made their final claim
+constexpr int CTR_FINAL = 2;         // total claims of the last dynamic run
+constexpr int CTR_RUNS = 3;          // dynamic runs completed
+constexpr int CTR_XCD = 4;           // [4, 12): per-XCD claim counters
+constexpr int CTR_WORDS = CTR_XCD + NUM_XCD;
+
+// Tiles are numbered along a locality-friendly order ("positions", see
+// tile_position below); a scheduler hands out positions. Split [0, n) into
+// `parts` contiguous nearly equal ranges; part p starts at part_begin(p).
+__device__ __forceinline__ int part_begin(int n, int parts, int p)
+{
+    const int q = n / parts, rem = n % parts;
+    return p * q + min(p, rem);
+}
+
+// Static grid-stride deals worker w the logical tiles w, w+P, w+2P, ...
+// Workgroups are dispatched to the XCDs round-robin, so in every round of P
+// logical tiles the workers of XCD x hold the logical tiles = x (mod 8).
+// This bijection of each round onto itself gives those workers consecutive
+// positions, i.e. one compact block of the output per XCD and round, whose
+// A and B panels that XCD's L2 then shares. It only permutes which tile a
+// logical index denotes; every position is still used exactly once.
+__device__ __forceinline__ int static_position(int t, int num_tiles, int num_workers)
+{
+    const int base = (t / num_workers) * num_workers;
+    const int r = min(num_workers, num_tiles - base);
+    const int u = t - base;
+    return base + part_begin(r, NUM_XCD, u % NUM_XCD) + u / NUM_XCD;
+}
+
+
+
+// A worker's tile sequence. `claim` is the scheduler's own value (the
+// logical index for static, the counter value for dynamic) and `pos` the
+// tile position it denotes; pos >= num_tiles means there is no more work.
+struct Claimed {
+    int32_t claim;
+    int32_t pos;
+};
+
 struct TileScheduler {
     uint32_t *counters;
     int32_t num_tiles;
     int32_t num_workers;
     int32_t worker;
     int32_t mode;
-    int32_t *slots; // two LDS words, alternating by tile sequence parity
-    uint32_t pending; // claim result, held by the leader lane until published
+    int32_t *slots;   // four LDS words: two (claim, pos) pairs, alternating by tile parity
+    int32_t xcd;      // this worker's XCD (dynamic XCD mode)
+    uint32_t pending; // raw counter value of the request in flight (leader lane)
 
-    __device__ __forceinline__ int32_t claim()
+    __device__ __forceinline__ uint32_t atomic_take(int idx)
     {
-        uint32_t v = __hip_atomic_fetch_add(counters, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return v > 0x7FFFFFFFu ? 0x7FFFFFFF : (int32_t)v;
+        return __hip_atomic_fetch_add(counters + idx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // Issue a request (leader lane only): one atomic on the single counter,
+    // or on this XCD's counter. Its value is read only in resolve().
+    __device__ __forceinline__ void issue()
+    {
+        pending = atomic_take(mode == SCHED_DYNAMIC ? CTR_CLAIM : CTR_XCD + xcd);
+    }
+
+    // Turn the request into a tile (leader lane only). Single counter: the
+    // counter value is the position. Per-XCD counters: this XCD's range
+    // first; once it is used up, take from the other XCDs' ranges in turn;
+    // only when every range is used up has the request failed.
+    __device__ __forceinline__ Claimed resolve()
+    {
+        if (mode == SCHED_DYNAMIC) {
+            const int32_t c = pending > 0x7FFFFFFFu ? 0x7FFFFFFF : (int32_t)pending;
+            return Claimed{c, c};
+        }
+        uint32_t v = pending;
+#pragma unroll 1
+        for (int d = 0; d < NUM_XCD; ++d) {
+            const int x = (xcd + d) % NUM_XCD;
+            const int lo = part_begin(num_tiles, NUM_XCD, x), hi = part_begin(num_tiles, NUM_XCD, x + 1);
+            if (d > 0)
+                v = atomic_take(CTR_XCD + x);
+            if (v < (uint32_t)(hi - lo))
+                return Claimed{(int32_t)(x * 0x1000000 + v), lo + (int32_t)v};
+        }
+        return Claimed{0x7FFFFFFF, num_tiles};
+    }
+
+    __device__ __forceinline__ Claimed publish_and_read(bool leader, int slot)
+    {
+        if (leader) {
+            const Claimed c = resolve();
+            slots[2 * slot] = c.claim;
+            slots[2 * slot + 1] = c.pos;
+        }
+        barrier_lds();
+        return Claimed{uniform(slots[2 * slot]), uniform(slots[2 * slot + 1])};
     }
 
     // First tile of this worker; all threads of the workgroup call it.
-    __device__ __forceinline__ int32_t first(bool leader)
+    __device__ __forceinline__ Claimed first(bool leader)
     {
-        if (mode == SCHED_STATIC)
-            return worker;
+        if (mode == SCHED_STATIC) {
+            const int32_t t = worker;
+            return Claimed{t, t < num_tiles ? static_position(t, num_tiles, num_workers) : num_tiles};
+        }
         if (leader)
-            slots[0] = claim();
-        barrier_lds();
-        return uniform(slots[0]);
+            issue();
+        return publish_and_read(leader, 0);
     }
 
     // Issue the request for the tile after the current one (leader only).
     __device__ __forceinline__ void claim_ahead(bool leader)
     {
-        if (mode == SCHED_DYNAMIC && leader)
-            pending = (uint32_t)claim();
+        if (mode != SCHED_STATIC && leader)
+            issue();
     }
 
-    // Make the pending claim visible to the workgroup. Must be followed by a
-    // barrier_lds() before next() reads it. `seq` is the current tile's
-    // position in this worker's sequence.
-    __device__ __forceinline__ void publish(bool leader, int seq)
+    // The tile after `current` (all threads). For dynamic modes the pending
+    // claim is resolved and published through LDS, which includes a barrier.
+    // `seq` is the current tile's position in this worker's sequence.
+    __device__ __forceinline__ Claimed next(Claimed current, bool leader, int seq)
     {
-        if (mode == SCHED_DYNAMIC && leader)
-            slots[(seq + 1) & 1] = (int32_t)pending;
-    }
-
-    __device__ __forceinline__ int32_t next(int32_t current, int seq)
-    {
-        if (mode == SCHED_STATIC)
-            return current + num_workers;
-        return uniform(slots[(seq + 1) & 1]);
+        if (mode == SCHED_STATIC) {
+            const int32_t t = current.claim + num_workers;
+            return Claimed{t, t < num_tiles ? static_position(t, num_tiles, num_workers) : num_tiles};
+        }
+        return publish_and_read(leader, (seq + 1) & 1);
     }
 
     // End-of-kernel bookkeeping (leader only; after the worker's failed claim).
     __device__ __forceinline__ void finish(bool leader)
     {
-        if (mode != SCHED_DYNAMIC || !leader)
+        if (mode == SCHED_STATIC || !leader)
             return;
-        uint32_t old = __hip_atomic_fetch_add(counters + 1, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t old = __hip_atomic_fetch_add(counters + CTR_EXIT, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         if (old == (uint32_t)num_workers - 1u) {
-            uint32_t final_claims = __hip_atomic_exchange(counters, 0u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(counters + 2, final_claims, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_add(counters + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(counters + 1, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t total = __hip_atomic_exchange(counters + CTR_CLAIM, 0u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            for (int x = 0; x < NUM_XCD; ++x)
+                total += __hip_atomic_exchange(counters + CTR_XCD + x, 0u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(counters + CTR_FINAL, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(counters + CTR_RUNS, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(counters + CTR_EXIT, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 };

@@ -130,8 +130,9 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
         return fail(GEMM_ERR_UNSUPPORTED, "A and B must be bf16 and the accumulator fp32");
     if (desc->dtype_d != GEMM_DTYPE_F32 && desc->dtype_d != GEMM_DTYPE_BF16)
         return fail(GEMM_ERR_UNSUPPORTED, "D must be fp32 or bf16");
-    if (desc->schedule != GEMM_SCHEDULE_STATIC && desc->schedule != GEMM_SCHEDULE_DYNAMIC)
-        return fail(GEMM_ERR_INVALID_VALUE, "schedule must be static (0) or dynamic (1)");
+    if (desc->schedule != GEMM_SCHEDULE_STATIC && desc->schedule != GEMM_SCHEDULE_DYNAMIC &&
+        desc->schedule != GEMM_SCHEDULE_DYNAMIC_XCD)
+        return fail(GEMM_ERR_INVALID_VALUE, "schedule must be static (0), dynamic (1) or dynamic per XCD (2)");
     if (desc->num_workers < 0)
         return fail(GEMM_ERR_INVALID_VALUE, "num_workers must be >= 0");
     if (desc->flags != GEMM_FLAG_NONE)
@@ -199,9 +200,9 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
         gd.ldd = s.ldd;
         if (s.m > 0 && s.n > 0)
             tiles += ceil_div(s.m, tm) * ceil_div(s.n, tn);
-        if (tiles > INT32_MAX / 2) {
+        if (tiles >= (int64_t)1 << 27) {
             delete plan;
-            return fail(GEMM_ERR_UNSUPPORTED, "more than 2^30 output tiles");
+            return fail(GEMM_ERR_UNSUPPORTED, "more than 2^27 output tiles");
         }
     }
 
@@ -401,7 +402,8 @@ gemm_status pts_sched_probe(int32_t num_tiles, int32_t num_workers, int32_t sche
 {
     if (num_tiles < 0 || num_workers < 1 || num_workers > 4096 || max_per_worker < 1)
         return fail(GEMM_ERR_INVALID_VALUE, "bad probe sizes");
-    if (schedule != GEMM_SCHEDULE_STATIC && schedule != GEMM_SCHEDULE_DYNAMIC)
+    if (schedule != GEMM_SCHEDULE_STATIC && schedule != GEMM_SCHEDULE_DYNAMIC &&
+        schedule != GEMM_SCHEDULE_DYNAMIC_XCD)
         return fail(GEMM_ERR_INVALID_VALUE, "bad schedule");
     if (gate_worker >= num_workers || work_ns < 0 || spin_limit < 0 || work_ns > 1000000000LL)
         return fail(GEMM_ERR_INVALID_VALUE, "bad probe parameters");

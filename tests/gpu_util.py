@@ -67,6 +67,22 @@ def check_close(d: torch.Tensor, ref: np.ndarray, k: int, what: str) -> float:
     return err
 
 
+def check_counters(schedule, counters, tiles, workers):
+    """Claim counters after a finished run: the live counters are back at zero.
+
+    Single counter: every worker's loop ends on exactly one failed claim, so a
+    run takes tiles + workers claims. Per-XCD counters: a request may also fail
+    on several XCD ranges before it finds a tile, so at least that many.
+    """
+    if schedule == "static":
+        return
+    assert counters[:2] == [0, 0], f"live counters not reset: {counters}"
+    if schedule == "dynamic":
+        assert counters[2] == tiles + workers, f"{counters[2]} claims, want {tiles + workers}"
+    else:
+        assert tiles + workers <= counters[2] <= tiles + 8 * (tiles + workers), counters
+
+
 def run_single(m, n, k, a, b, out_dtype, schedule, tile=(0, 0), lda=0, ldb=0, ldd=0, num_workers=0, d=None):
     """One plan, one run; D defaults to a NaN-filled (m x ldd) buffer. ld = 0 is packed."""
     import persistent_tile_scheduling_amd as pts

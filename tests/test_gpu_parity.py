@@ -7,7 +7,8 @@ Bars (the tolerance is written here, per case):
   1e-2 sqrt(K) (bf16 output), over every element at oracle-sized shapes and
   over sampled entries (every tile's four corners plus random entries) at the
   full configuration sizes;
-* static and dynamic schedules -- bitwise identical D (same tile body).
+* static, dynamic and per-XCD dynamic schedules -- bitwise identical D
+  (same tile body).
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-BOTH = ("static", "dynamic")
+SCHEDULES = ("static", "dynamic", "dynamic_xcd")
 
 
 @pytest.fixture(scope="module")
@@ -52,14 +53,15 @@ def test_config1_256_cube_fp32_64x64(pts):
     ref = oracle.gemm(a_bits, b_bits, m, n, k)
     a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
     outs = {}
-    for sched in BOTH:
+    for sched in SCHEDULES:
         U.log(f"config1 256^3 fp32 tile 64x64 schedule={sched}")
         d, counters, (tiles, workers) = U.run_single(m, n, k, a, b, torch.float32, sched, tile=(64, 64))
         assert (tiles, workers) == (16, 16)
         err = U.check_close(d, ref, k, f"config1 {sched}")
         U.log(f"  max err {err:.3g} (tol {U.tol_for(torch.float32, k):.3g})")
         outs[sched] = d
-    assert torch.equal(outs["static"], outs["dynamic"])
+    for sched in SCHEDULES[1:]:
+        assert torch.equal(outs["static"], outs[sched])
 
 
 # ---------------------------------------------------------------------------
@@ -84,7 +86,7 @@ def test_integer_exact_sweep(pts, tile, out_dtype):
         a_bits, b_bits = _operands(m, n, k, 3, kind="integer", lda=lda, ldb=ldb)
         ref = oracle.gemm(a_bits, b_bits, m, n, k, lda=lda, ldb=ldb)
         a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
-        for sched in BOTH:
+        for sched in SCHEDULES:
             U.log(f"integer sweep {(m, n, k)} tile {tile} {out_dtype} {sched}")
             d, _, _ = U.run_single(m, n, k, a, b, out_dtype, sched, tile=tile, lda=lda, ldb=ldb)
             U.check_exact(d[:m, :n], ref, f"{(m, n, k)} tile {tile} {sched}")
@@ -106,7 +108,7 @@ def test_random_ragged_full_oracle(pts, shape, out_dtype, tile):
     ref = oracle.gemm(a_bits, b_bits, m, n, k, lda=lda, ldb=ldb)
     a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
     outs = {}
-    for sched in BOTH:
+    for sched in SCHEDULES:
         U.log(f"ragged {shape} {out_dtype} {sched}")
         d = torch.full((m + 3, ldd), 7.0, dtype=out_dtype, device=U.DEV)
         U.run_single(m, n, k, a, b, out_dtype, sched, tile=tile, lda=lda, ldb=ldb, ldd=ldd, d=d)
@@ -114,7 +116,8 @@ def test_random_ragged_full_oracle(pts, shape, out_dtype, tile):
         assert torch.all(d[:m, n:] == 7.0), "row padding of D was written"
         assert torch.all(d[m:] == 7.0), "rows past M were written"
         outs[sched] = d
-    assert torch.equal(outs["static"], outs["dynamic"])
+    for sched in SCHEDULES[1:]:
+        assert torch.equal(outs["static"], outs[sched])
 
 
 def test_identity_reproduces_a(pts):
@@ -123,7 +126,7 @@ def test_identity_reproduces_a(pts):
     b_bits = np.zeros((k, k), np.uint16)
     np.fill_diagonal(b_bits, 0x3F80)
     a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
-    for sched in BOTH:
+    for sched in SCHEDULES:
         d, _, _ = U.run_single(m, k, k, a, b, torch.bfloat16, sched)
         assert np.array_equal(U.device_to_bits(d), a_bits), "A . I != A (bf16 output)"
 
@@ -147,7 +150,7 @@ def test_ones_closed_form_rne(pts):
 # ---------------------------------------------------------------------------
 
 def test_k_zero_writes_zeros(pts):
-    for sched in BOTH:
+    for sched in SCHEDULES:
         d, _, (tiles, _) = U.run_single(300, 200, 0, None, None, torch.float32, sched)
         assert tiles == 2
         assert torch.all(d == 0)
@@ -169,7 +172,7 @@ def test_tile_reuse_does_not_accumulate_across_tiles(pts):
     a_bits, b_bits = _operands(m, n, k, 13, kind="integer")
     ref = oracle.gemm(a_bits, b_bits, m, n, k)
     a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
-    for sched in BOTH:
+    for sched in SCHEDULES:
         d, _, (tiles, workers) = U.run_single(m, n, k, a, b, torch.float32, sched, tile=(128, 128), num_workers=1)
         assert (tiles, workers) == (16, 1)
         U.check_exact(d, ref, f"single worker {sched}")
@@ -180,7 +183,7 @@ def test_more_workers_than_tiles(pts):
     a_bits, b_bits = _operands(m, n, k, 2, kind="integer")
     ref = oracle.gemm(a_bits, b_bits, m, n, k)
     a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
-    for sched in BOTH:
+    for sched in SCHEDULES:
         d, counters, (tiles, workers) = U.run_single(m, n, k, a, b, torch.float32, sched, tile=(64, 64),
                                                      num_workers=9)
         assert (tiles, workers) == (4, 9)
@@ -203,7 +206,7 @@ def test_grouped_small_full_oracle(pts):
         tensors.append((U.bits_to_device(a_bits), U.bits_to_device(b_bits),
                         torch.full((max(m, 1), n), float("nan"), dtype=torch.bfloat16, device=U.DEV)))
     outs = {}
-    for sched in BOTH:
+    for sched in SCHEDULES:
         U.log(f"grouped small {sched}")
         for (_, _, d) in tensors:
             d.fill_(float("nan"))
@@ -215,8 +218,9 @@ def test_grouped_small_full_oracle(pts):
             if m:
                 U.check_close(d[:m], refs[g], k, f"group {g} {sched}")
         outs[sched] = [d.clone() for (_, _, d) in tensors]
-    for x, y in zip(outs["static"], outs["dynamic"]):
-        assert torch.equal(x.nan_to_num(0.0), y.nan_to_num(0.0))
+    for sched in SCHEDULES[1:]:
+        for x, y in zip(outs["static"], outs[sched]):
+            assert torch.equal(x.nan_to_num(0.0), y.nan_to_num(0.0))
 
 
 # ---------------------------------------------------------------------------
@@ -229,15 +233,15 @@ def _single_full(pts, m, n, k, out_dtype, seed=0):
     (rows, cols), = U.sample_entries([(m, n)], 256, 256, 2048, seed=seed)
     ref = U.oracle_sampled(seed, gen.TENSOR_A, gen.TENSOR_B, k, rows, cols)
     outs = {}
-    for sched in BOTH:
+    for sched in SCHEDULES:
         U.log(f"full {m}x{n}x{k} {out_dtype} {sched}")
         d, counters, (tiles, workers) = U.run_single(m, n, k, a, b, out_dtype, sched)
         err = U.check_sampled(d, rows, cols, ref, k, f"{m}x{n}x{k} {sched}")
         U.log(f"  sampled max err {err:.3g} (tol {U.tol_for(out_dtype, k):.3g}), tiles {tiles} workers {workers}")
-        if sched == "dynamic":
-            assert counters[:3] == [0, 0, tiles + workers]
+        U.check_counters(sched, counters, tiles, workers)
         outs[sched] = d
-    assert torch.equal(outs["static"], outs["dynamic"])
+    for sched in SCHEDULES[1:]:
+        assert torch.equal(outs["static"], outs[sched])
     U.check_against_fp32_matmul(outs["dynamic"], a, b, k, f"{m}x{n}x{k}")
 
 
@@ -269,20 +273,20 @@ def test_config4_grouped_64_problems_sampled(pts):
         ta, tb = gen.group_tensor_ids(g)
         refs.append(U.oracle_sampled(seed, ta, tb, k, rows, cols))
     outs = {}
-    for sched in BOTH:
+    for sched in SCHEDULES:
         U.log(f"config4 grouped {sched} sum(M)={sum(ms)}")
         with pts.Plan(shapes, torch.bfloat16, schedule=sched) as p:
             p.run(tensors)
             torch.cuda.synchronize()
-            if sched == "dynamic":
-                assert p.counters()[:3] == [0, 0, p.num_tiles + p.num_workers]
+            U.check_counters(sched, p.counters(), p.num_tiles, p.num_workers)
         worst = 0.0
         for g, ((rows, cols), ref) in enumerate(zip(samples, refs)):
             worst = max(worst, U.check_sampled(tensors[g][2], rows, cols, ref, k, f"config4 group {g} {sched}"))
         U.log(f"  sampled max err {worst:.3g}")
         outs[sched] = [t[2].clone() for t in tensors]
-    for x, y in zip(outs["static"], outs["dynamic"]):
-        assert torch.equal(x, y)
+    for sched in SCHEDULES[1:]:
+        for x, y in zip(outs["static"], outs[sched]):
+            assert torch.equal(x, y)
 
 
 def test_config5_with_concurrent_copy_sampled(pts):
@@ -298,7 +302,7 @@ def test_config5_with_concurrent_copy_sampled(pts):
     dst = torch.zeros(ncopy + 64, dtype=torch.int16, device=U.DEV)
     copy_stream = torch.cuda.Stream()
     outs = {}
-    for sched in BOTH:
+    for sched in SCHEDULES:
         U.log(f"config5 {sched} with concurrent copy")
         dst.zero_()
         d = torch.empty((m, n), dtype=torch.bfloat16, device=U.DEV)
@@ -311,4 +315,5 @@ def test_config5_with_concurrent_copy_sampled(pts):
         assert torch.equal(dst[:ncopy], src), "copy result differs"
         assert torch.all(dst[ncopy:] == 0), "copy wrote past the end"
         outs[sched] = d
-    assert torch.equal(outs["static"], outs["dynamic"])
+    for sched in SCHEDULES[1:]:
+        assert torch.equal(outs["static"], outs[sched])

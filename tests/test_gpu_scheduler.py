@@ -6,9 +6,13 @@
   (tests/golden), also when worker 3 starts only after the others finished
   (the launch tail: it still owns 3, 7, 11). Dynamic claiming must process
   every tile exactly once and leave nothing for the late worker.
+* Per-XCD claiming (one counter per XCD over a contiguous range of tile
+  positions, stealing from the other ranges once the own one is used up) must
+  also hand out every position exactly once; a worker only moves on to a
+  range farther from its own XCD, and inside a range its claims increase.
 * The GEMM kernel's own per-tile trace must cover every output tile of the
   problem exactly once, follow the static assignment in static mode, and end
-  each dynamic run with the claim counter at tiles + workers.
+  each dynamic run with the claim counters reset.
 """
 from __future__ import annotations
 
@@ -47,7 +51,7 @@ def _probe(pts, tiles, workers, schedule, gate=-1, work_ns=20000, maxpw=None, co
     out = torch.full((workers, maxpw), -1, dtype=torch.int32, device=U.DEV)
     counts = torch.full((workers,), -1, dtype=torch.int32, device=U.DEV)
     if counters is None:
-        counters = torch.zeros(8, dtype=torch.int32, device=U.DEV)
+        counters = torch.zeros(16, dtype=torch.int32, device=U.DEV)
     status = torch.zeros(1, dtype=torch.int32, device=U.DEV)
     pts.pts_sched_probe(tiles, workers, schedule, gate, work_ns, 2_000_000, out, counts, maxpw, counters, status)
     torch.cuda.synchronize()
@@ -85,7 +89,7 @@ def test_probe_dynamic_late_worker_finds_nothing(pts):
 
 def test_probe_dynamic_at_scale_and_repeated(pts):
     # one counter block across runs: each run must leave it reset for the next
-    shared = torch.zeros(8, dtype=torch.int32, device=U.DEV)
+    shared = torch.zeros(16, dtype=torch.int32, device=U.DEV)
     for run in range(3):
         per_worker, counters = _probe(pts, 4096, 256, pts.GEMM_SCHEDULE_DYNAMIC, work_ns=2000, counters=shared)
         oracle.check_dynamic_claims(per_worker, 4096)
@@ -95,6 +99,44 @@ def test_probe_dynamic_at_scale_and_repeated(pts):
 def test_probe_static_at_scale(pts):
     per_worker, _ = _probe(pts, 1000, 256, pts.GEMM_SCHEDULE_STATIC, work_ns=1000)
     assert per_worker == oracle.static_assignment(1000, 256)
+
+
+def _xcd_range(num_tiles, x):
+    q, rem = divmod(num_tiles, 8)
+    lo = x * q + min(x, rem)
+    return lo, lo + q + (1 if x < rem else 0)
+
+
+def check_xcd_claims(claims, worker_xcd, num_tiles):
+    """Per-XCD claiming: `claims` per worker are XCD * 2^24 + counter value."""
+    positions = []
+    for w, seq in enumerate(claims):
+        dists, last = [], {}
+        for c in seq:
+            x, v = c >> 24, c & 0xFFFFFF
+            lo, hi = _xcd_range(num_tiles, x)
+            assert 0 <= x < 8 and lo + v < hi, f"worker {w}: claim {c} outside XCD {x}'s range"
+            positions.append(lo + v)
+            assert v > last.get(x, -1), f"worker {w}: claims in XCD {x}'s range not increasing"
+            last[x] = v
+            dists.append((x - worker_xcd[w]) % 8)
+        assert dists == sorted(dists), f"worker {w} went back to a nearer XCD range: {dists}"
+    assert sorted(positions) == list(range(num_tiles)), "positions not covered exactly once"
+    return positions
+
+
+def test_probe_dynamic_xcd_exactly_once(pts):
+    for tiles, workers, work in ((12, 4, 20000), (4096, 256, 2000), (1000, 256, 500), (7, 9, 1000)):
+        per_worker, counters = _probe(pts, tiles, workers, pts.GEMM_SCHEDULE_DYNAMIC_XCD, work_ns=work)
+        assert sorted(t for ts in per_worker for t in ts) == list(range(tiles))
+        assert counters[:2] == [0, 0] and counters[4:12] == [0] * 8
+        assert counters[2] >= tiles + workers
+
+
+def test_probe_dynamic_xcd_late_worker_finds_nothing(pts):
+    per_worker, counters = _probe(pts, 12, 4, pts.GEMM_SCHEDULE_DYNAMIC_XCD, gate=3)
+    assert sorted(t for ts in per_worker for t in ts) == list(range(12))
+    assert per_worker[3] == []
 
 
 def _traced_run(pts, shapes, schedule, tile=(0, 0), num_workers=0, out_dtype=torch.float32, k=64):
@@ -112,26 +154,39 @@ def _traced_run(pts, shapes, schedule, tile=(0, 0), num_workers=0, out_dtype=tor
         return tiles.copy(), workers.copy(), p.num_tiles, p.num_workers, p.counters()
 
 
-@pytest.mark.parametrize("schedule", ["static", "dynamic"])
+@pytest.mark.parametrize("schedule", ["static", "dynamic", "dynamic_xcd"])
 @pytest.mark.parametrize("shapes,tile", [([(5000, 7000)], (256, 256)), ([(256, 256)], (64, 64)),
-                                         ([(300, 200), (0, 10), (1000, 64), (1, 1)], (128, 128))])
+                                         ([(300, 200), (0, 10), (1000, 64), (1, 1)], (128, 128)),
+                                         ([(20000, 2048)], (256, 256))])
 def test_gemm_trace_covers_every_tile_once(pts, schedule, shapes, tile):
     tiles, workers, nt, nw, counters = _traced_run(pts, shapes, schedule, tile)
+    # every output tile of every problem exactly once ...
     want = sorted((g, r0, c0) for (g, r0, c0, _, _) in oracle.tile_coords(shapes, *tile))
     got = sorted(zip(tiles["group"].tolist(), tiles["row0"].tolist(), tiles["col0"].tolist()))
     assert got == want
+    # ... and every tile position exactly once
     assert sorted(tiles["tile"].tolist()) == list(range(nt))
+    order = np.lexsort((tiles["seq"], tiles["worker"]))
     per_worker = [[] for _ in range(nw)]
-    for rec in sorted(tiles.tolist(), key=lambda r: (r[1], r[2])):
-        per_worker[rec[1]].append(rec[0])
+    for i in order:
+        per_worker[tiles["worker"][i]].append(int(tiles["claim"][i]))
     assert [len(p) for p in per_worker] == workers["tiles"].tolist()
+    for w, p in enumerate(per_worker):
+        seqs = sorted(int(x) for x in tiles["seq"][tiles["worker"] == w])
+        assert seqs == list(range(len(p)))
     assert workers["worker"].tolist() == list(range(nw))
     assert np.all(tiles["t_end"] >= tiles["t_start"])
+    assert np.all(tiles["xcc_id"] == workers["xcc_id"][tiles["worker"]])
     if schedule == "static":
         assert per_worker == oracle.static_assignment(nt, nw)
-    else:
+    elif schedule == "dynamic":
+        assert np.array_equal(tiles["claim"], tiles["tile"])
         oracle.check_dynamic_claims(per_worker, nt)
-        assert counters[:3] == [0, 0, nt + nw]
+    else:
+        positions = check_xcd_claims(per_worker, (workers["xcc_id"] % 8).tolist(), nt)
+        flat = [tiles["tile"][i] for i in order]
+        assert positions == [int(t) for t in flat]
+    U.check_counters(schedule, counters, nt, nw)
 
 
 def test_copy_kernel(pts):
