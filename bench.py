@@ -67,25 +67,52 @@ def make_operands(wl, seed=0):
     return ops
 
 
-def time_schedule(pts, wl, ops, schedule, steps, warmup, copy_bufs=None):
+class Concurrent:
+    """The concurrent HBM-bound load of the copy workload: a grid-stride int16
+    copy launched just before each GEMM run on a second stream. With
+    copy_cus > 0 that stream is restricted to the first copy_cus compute
+    units, so the copy holds part of the chip and the GEMM workers placed
+    there start late."""
+
+    def __init__(self, pts, n, copy_cus):
+        import pts_inputs as gen
+        import torch
+        self.pts = pts
+        self.n = n
+        self.src = gen.uniform_bf16_torch(n, 0, gen.TENSOR_COPY_SRC, "cuda").view(torch.int16)
+        self.dst = torch.empty_like(self.src)
+        self.raw = pts.pts_stream_create_cu_masked(copy_cus) if copy_cus > 0 else None
+        self.stream = self.raw if self.raw is not None else torch.cuda.Stream()
+        self.blocks = 4 * copy_cus if copy_cus > 0 else 0
+
+    def launch(self):
+        self.pts.pts_copy_int16(self.src, self.dst, self.n, self.blocks, self.stream)
+
+    def close(self):
+        import torch
+        torch.cuda.synchronize()
+        if self.raw is not None:
+            self.pts.pts_stream_destroy(self.raw)
+            self.raw = None
+
+
+def time_headline(pts, wl, ops, schedule, steps, warmup, conc=None):
+    """K timed steps of one schedule, wall clock plus per-launch HIP events."""
     import torch
     stream = torch.cuda.Stream()
-    copy_stream = torch.cuda.Stream() if copy_bufs is not None else None
     flops = sum(2.0 * m * n * k for (m, n, k) in wl["shapes"])
     with pts.Plan(wl["shapes"], wl["out"], wl["tile"], schedule) as plan:
-        def one():
-            if copy_bufs is not None:
-                pts.pts_copy_int16(copy_bufs[0], copy_bufs[1], copy_bufs[0].numel(), 0, copy_stream)
-            plan.run(ops, stream)
         for _ in range(warmup):
-            one()
+            if conc is not None:
+                conc.launch()
+            plan.run(ops, stream)
         torch.cuda.synchronize()
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         t0 = time.perf_counter()
         for i in range(steps):
-            if copy_bufs is not None:
-                pts.pts_copy_int16(copy_bufs[0], copy_bufs[1], copy_bufs[0].numel(), 0, copy_stream)
+            if conc is not None:
+                conc.launch()
             starts[i].record(stream)
             plan.run(ops, stream)
             ends[i].record(stream)
@@ -93,32 +120,66 @@ def time_schedule(pts, wl, ops, schedule, steps, warmup, copy_bufs=None):
         wall = time.perf_counter() - t0
         kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
         info = dict(num_tiles=plan.num_tiles, num_workers=plan.num_workers, lds_bytes=plan.lds_bytes)
-    kms_sorted = sorted(kms)
     avg = sum(kms) / len(kms)
     return dict(
         schedule=schedule,
         ms_per_step=wall * 1e3 / steps,
         tflops=flops * steps / wall / 1e12,
         kernel_ms_avg=avg,
-        kernel_ms_median=kms_sorted[len(kms) // 2],
-        kernel_ms_min=kms_sorted[0],
+        kernel_ms_median=sorted(kms)[len(kms) // 2],
+        kernel_ms_min=min(kms),
         kernel_tflops=flops / (avg * 1e-3) / 1e12,
-        frac_of_peak=flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         **info,
     ), flops
 
 
-def tail_idle(pts, wl, ops, schedule, copy_bufs=None):
+def compare_schedules(pts, wl, ops, schedules, rounds, conc=None):
+    """Every schedule run in turn, `rounds` times, the order rotated each round,
+    so that clock and power drift fall on all schedules alike. Kernel times
+    from HIP events on the launch stream; medians reported."""
+    import torch
+    stream = torch.cuda.Stream()
+    flops = sum(2.0 * m * n * k for (m, n, k) in wl["shapes"])
+    plans = {s: pts.Plan(wl["shapes"], wl["out"], wl["tile"], s) for s in schedules}
+    times = {s: [] for s in schedules}
+    try:
+        for s in schedules:
+            if conc is not None:
+                conc.launch()
+            plans[s].run(ops, stream)
+        torch.cuda.synchronize()
+        for r in range(rounds):
+            order = schedules[r % len(schedules):] + schedules[:r % len(schedules)]
+            for s in order:
+                if conc is not None:
+                    conc.launch()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                plans[s].run(ops, stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times[s].append(e0.elapsed_time(e1))
+    finally:
+        for p in plans.values():
+            p.close()
+    out = {}
+    for s, ts in times.items():
+        med = sorted(ts)[len(ts) // 2]
+        out[s] = dict(kernel_ms_median=med, kernel_ms_min=min(ts), kernel_tflops_median=flops / (med * 1e-3) / 1e12)
+    return out
+
+
+def tail_idle(pts, wl, ops, schedule, conc=None):
     """Fraction of worker-time idle after each worker's last tile, from the trace."""
     import torch
     stream = torch.cuda.Stream()
-    copy_stream = torch.cuda.Stream() if copy_bufs is not None else None
     with pts.Plan(wl["shapes"], wl["out"], wl["tile"], schedule) as plan:
         buf = torch.zeros(plan.trace_bytes() // 4 + 4, dtype=torch.int32, device="cuda")
         plan.set_trace(buf)
         for _ in range(2):
-            if copy_bufs is not None:
-                pts.pts_copy_int16(copy_bufs[0], copy_bufs[1], copy_bufs[0].numel(), 0, copy_stream)
+            if conc is not None:
+                conc.launch()
             plan.run(ops, stream)
         torch.cuda.synchronize()
         tiles, workers = pts.decode_trace(buf, plan.num_tiles, plan.num_workers)
@@ -130,6 +191,40 @@ def tail_idle(pts, wl, ops, schedule, copy_bufs=None):
     per = workers["tiles"]
     return dict(tail_idle_frac=idle, late_start_frac=late, span_us=span / 100.0,
                 tiles_per_worker_min=int(per.min()), tiles_per_worker_max=int(per.max()))
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources the GEMM kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    base = os.path.join(ROOT, "persistent_tile_scheduling_amd", "csrc")
+    for dirpath, _, files in sorted(os.walk(base)):
+        for f in sorted(files):
+            if f.endswith((".h", ".hip")):
+                path = os.path.join(dirpath, f)
+                h.update(os.path.relpath(path, base).encode())
+                h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name, schedule, wl):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload and schedule, or None when there is none or the kernel
+    sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"gemm_{workload_name}_{schedule}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#")):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl, budget_s: float):
@@ -160,8 +255,8 @@ def cpu_baseline(wl, budget_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--schedules", default="static,dynamic,dynamic_xcd")
     ap.add_argument("--tile-k", type=int, default=0, help="k-tile depth (0 = library default)")
@@ -171,6 +266,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
+    ap.add_argument("--compare-rounds", type=int, default=10,
+                    help="interleaved rounds of every schedule for the comparison (0 = skip)")
+    ap.add_argument("--copy-cus", type=int, default=64,
+                    help="compute units the concurrent copy may use (0 = all, unmasked stream)")
     ap.add_argument("--calibration-copy", type=int, default=0,
                     help="also run one int16 copy of this many elements (PMC calibration)")
     args = ap.parse_args()
@@ -190,11 +289,7 @@ def main():
     wl["tile"] = tuple(wl["tile"][:2]) + (args.tile_k, args.stages, args.load_path, args.waves)
     print(f"# workload {args.workload}: {wl['desc']}", file=sys.stderr, flush=True)
     ops = make_operands(wl)
-    copy_bufs = None
-    if wl["copy"]:
-        import pts_inputs as gen
-        src = gen.uniform_bf16_torch(wl["copy"], 0, gen.TENSOR_COPY_SRC, "cuda").view(torch.int16)
-        copy_bufs = (src, torch.empty_like(src))
+    conc = Concurrent(pts, wl["copy"], args.copy_cus) if wl["copy"] else None
     torch.cuda.synchronize()
 
     if args.calibration_copy:
@@ -205,18 +300,27 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    schedules = args.schedules.split(",")
+    head_sched = "dynamic_xcd" if "dynamic_xcd" in schedules else schedules[-1]
+    head, flops = time_headline(pts, wl, ops, head_sched, args.steps, args.warmup, conc)
+    print(f"# headline {head_sched}: {head['tflops']:.1f} TFLOP/s wall, {head['kernel_tflops']:.1f} TFLOP/s "
+          f"kernel ({head['kernel_ms_avg']:.4f} ms avg), {100 * head['kernel_tflops'] / PEAK_BF16_TFLOPS:.1f}% "
+          f"of peak", file=sys.stderr, flush=True)
     results = {}
-    flops = None
-    for sched in args.schedules.split(","):
-        r, flops = time_schedule(pts, wl, ops, sched, args.steps, args.warmup, copy_bufs)
-        print(f"# {sched}: {r['kernel_tflops']:.1f} TFLOP/s kernel, {r['tflops']:.1f} TFLOP/s wall, "
-              f"{r['kernel_ms_avg']:.4f} ms avg kernel, {100 * r['frac_of_peak']:.1f}% of peak",
-              file=sys.stderr, flush=True)
-        if not args.no_trace:
-            r.update(tail_idle(pts, wl, ops, sched, copy_bufs))
-        results[sched] = r
+    if len(schedules) > 1 and args.compare_rounds > 0:
+        results = compare_schedules(pts, wl, ops, schedules, args.compare_rounds, conc)
+        for sched, r in results.items():
+            print(f"# compare {sched}: median {r['kernel_ms_median']:.4f} ms, {r['kernel_tflops_median']:.1f} "
+                  f"TFLOP/s", file=sys.stderr, flush=True)
+    if not args.no_trace:
+        for sched in schedules:
+            r = results.setdefault(sched, {})
+            r.update(tail_idle(pts, wl, ops, sched, conc))
+            print(f"# trace {sched}: tail idle {r['tail_idle_frac']:.3f}, late start {r['late_start_frac']:.3f}",
+                  file=sys.stderr, flush=True)
+    if conc is not None:
+        conc.close()
 
-    head = results.get("dynamic_xcd") or results.get("dynamic") or next(iter(results.values()))
     line = {
         "metric": METRIC,
         "value": round(head["tflops"], 2),
@@ -230,16 +334,22 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl["desc"], "schedule": head["schedule"],
+        "config": {"workload": wl["desc"], "schedule": head_sched,
                    "shapes": wl["shapes"] if len(wl["shapes"]) <= 4 else f"{len(wl['shapes'])} problems",
-                   "tile": list(wl["tile"]), "out_dtype": str(wl["out"]).replace("torch.", "")},
+                   "tile": list(wl["tile"]), "out_dtype": str(wl["out"]).replace("torch.", ""),
+                   "copy_cus": args.copy_cus if wl["copy"] else None},
         "roofline": {"bound": "mfma", "achieved": round(head["kernel_tflops"], 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
-                     "frac": round(head["kernel_tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "pts::gemm_persistent_kernel", "flop_per_launch": flops},
+                     "frac": round(head["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(args.workload, head_sched, wl),
+                     "kernel": "pts::gemm_persistent_kernel", "flop_per_launch": flops,
+                     "kernel_ms_avg": round(head["kernel_ms_avg"], 5)},
         "schedules": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in results.items()},
     }
+    if "static" in results and "kernel_ms_median" in results["static"]:
+        line["dynamic_vs_static"] = {s: round(results["static"]["kernel_ms_median"] / r["kernel_ms_median"], 4)
+                                     for s, r in results.items() if s != "static" and "kernel_ms_median" in r}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)

@@ -198,6 +198,19 @@ gemm_status gemm_plan_read_counters(const gemm_plan *plan, uint32_t out[4]);
 gemm_status pts_copy_int16(const void *src, void *dst, int64_t n, int32_t num_blocks, void *stream);
 
 /*
+ * A stream whose kernels run only on the first `cu_count` compute units of
+ * the current device (hipExtStreamCreateWithCUMask), default priority. It
+ * stands for "another kernel occupies part of the CUs" beside a GEMM ("Advanced
+ * scheduling: Cluster Launch Control", section "Limits of the static
+ * persistent scheduler"): a copy launched on it holds those CUs, so GEMM
+ * workers placed there start late. 1 <= cu_count <= compute units, else
+ * GEMM_ERR_INVALID_VALUE; *out_stream is NULL on error. Destroy it with
+ * pts_stream_destroy (NULL is a no-op) once its work has finished.
+ */
+gemm_status pts_stream_create_cu_masked(int32_t cu_count, void **out_stream);
+gemm_status pts_stream_destroy(void *stream);
+
+/*
  * Scheduler probe: runs the tile scheduler alone, with `work_ns` of busy-wait
  * standing in for each tile's work, one 64-thread workgroup per worker.
  * out_tiles[w * max_per_worker + i] receives the i-th tile worker w processed

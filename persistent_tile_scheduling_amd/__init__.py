@@ -81,6 +81,8 @@ def _load():
         "gemm_plan_set_trace": (ctypes.c_int, [P, P, ctypes.c_size_t]),
         "gemm_plan_read_counters": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_uint32)]),
         "pts_copy_int16": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32, P]),
+        "pts_stream_create_cu_masked": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(P)]),
+        "pts_stream_destroy": (ctypes.c_int, [P]),
         "pts_sched_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int64, ctypes.c_int64, P, P, ctypes.c_int32, P, P, P]),
     }
@@ -182,6 +184,17 @@ def gemm_plan_read_counters(plan: int) -> list[int]:
 def pts_copy_int16(src, dst, n: int, num_blocks: int = 0, stream=None) -> None:
     _check(_lib.pts_copy_int16(ctypes.c_void_p(_ptr(src)), ctypes.c_void_p(_ptr(dst)), n, num_blocks,
                                ctypes.c_void_p(_stream_handle(stream))))
+
+
+def pts_stream_create_cu_masked(cu_count: int) -> int:
+    """A raw stream handle whose kernels run only on the first cu_count CUs."""
+    out = ctypes.c_void_p()
+    _check(_lib.pts_stream_create_cu_masked(cu_count, ctypes.byref(out)))
+    return int(out.value)
+
+
+def pts_stream_destroy(stream: int) -> None:
+    _check(_lib.pts_stream_destroy(ctypes.c_void_p(stream)))
 
 
 def pts_sched_probe(num_tiles: int, num_workers: int, schedule: int, gate_worker: int, work_ns: int,

@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/pts_gemm.h: plan validation,
 // tile-space construction, plan-owned device memory, and kernel launches.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -394,6 +395,38 @@ gemm_status pts_copy_int16(const void *src, void *dst, int64_t n, int32_t num_bl
                        (const int4 *)src, (int4 *)dst, nvec, (const int16_t *)src, (int16_t *)dst, n);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? GEMM_OK : hip_fail(e, "copy launch");
+}
+
+gemm_status pts_stream_create_cu_masked(int32_t cu_count, void **out_stream)
+{
+    if (out_stream == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "NULL out_stream");
+    *out_stream = nullptr;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "device query");
+    if (cu_count < 1 || cu_count > cus)
+        return fail(GEMM_ERR_INVALID_VALUE, "cu_count must be in [1, compute units]");
+    std::vector<uint32_t> mask((cus + 31) / 32, 0u);
+    for (int c = 0; c < cu_count; ++c)
+        mask[c / 32] |= 1u << (c % 32);
+    hipStream_t st = nullptr;
+    e = hipExtStreamCreateWithCUMask(&st, (uint32_t)mask.size(), mask.data());
+    if (e != hipSuccess)
+        return hip_fail(e, "hipExtStreamCreateWithCUMask");
+    *out_stream = st;
+    return GEMM_OK;
+}
+
+gemm_status pts_stream_destroy(void *stream)
+{
+    if (stream == nullptr)
+        return GEMM_OK;
+    hipError_t e = hipStreamDestroy((hipStream_t)stream);
+    return e == hipSuccess ? GEMM_OK : hip_fail(e, "hipStreamDestroy");
 }
 
 gemm_status pts_sched_probe(int32_t num_tiles, int32_t num_workers, int32_t schedule, int32_t gate_worker,

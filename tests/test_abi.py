@@ -100,6 +100,8 @@ def test_null_arguments(binding):
     assert lib.pts_copy_int16(None, None, -1, 0, None) == binding.GEMM_ERR_INVALID_VALUE
     assert lib.pts_copy_int16(None, None, 0, 0, None) == binding.GEMM_OK     # empty copy is a no-op
     assert lib.pts_sched_probe(12, 0, 0, -1, 0, 0, None, None, 1, None, None, None) == 1
+    assert lib.pts_stream_create_cu_masked(4, None) == binding.GEMM_ERR_INVALID_VALUE
+    assert lib.pts_stream_destroy(None) == binding.GEMM_OK
     assert "NULL" in binding.gemm_last_error() or binding.gemm_last_error() != ""
 
 

@@ -300,20 +300,22 @@ def test_config5_with_concurrent_copy_sampled(pts):
     ncopy = 1 << 30
     src = gen.uniform_bf16_torch(ncopy, seed, gen.TENSOR_COPY_SRC, U.DEV).view(torch.int16)
     dst = torch.zeros(ncopy + 64, dtype=torch.int16, device=U.DEV)
-    copy_stream = torch.cuda.Stream()
+    # the copy holds 64 of the compute units while the GEMM runs
+    copy_stream = pts.pts_stream_create_cu_masked(64)
     outs = {}
     for sched in SCHEDULES:
-        U.log(f"config5 {sched} with concurrent copy")
+        U.log(f"config5 {sched} with concurrent copy on 64 CUs")
         dst.zero_()
         d = torch.empty((m, n), dtype=torch.bfloat16, device=U.DEV)
         torch.cuda.synchronize()
         with pts.Plan([(m, n, k)], torch.bfloat16, schedule=sched) as p:
-            pts.pts_copy_int16(src, dst, ncopy, 0, copy_stream)
+            pts.pts_copy_int16(src, dst, ncopy, 256, copy_stream)
             p.run([(a, b, d)])
             torch.cuda.synchronize()
         U.check_sampled(d, rows, cols, ref, k, f"config5 {sched}")
         assert torch.equal(dst[:ncopy], src), "copy result differs"
         assert torch.all(dst[ncopy:] == 0), "copy wrote past the end"
         outs[sched] = d
+    pts.pts_stream_destroy(copy_stream)
     for sched in SCHEDULES[1:]:
         assert torch.equal(outs["static"], outs[sched])
