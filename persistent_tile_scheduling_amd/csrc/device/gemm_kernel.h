@@ -9,9 +9,9 @@
 //       --(ds_read_b128 fragments)--> v_mfma_f32_32x32x16_bf16, fp32 in AGPRs
 //       --(masked epilogue, fp32 or bf16 round-to-nearest-even)--> D
 //
-// Workgroup: 4 waves in a 2 x 2 grid; each wave owns a (BM/2) x (BN/2) block
-// of the output tile and, for every k-tile, issues its quarter of the ring
-// stage's loads. Load and compute overlap through the ring: while stage s is
+// Workgroup: WAVES_M x WAVES_N waves (2 x 2, or 2 x 4 for two waves per SIMD);
+// each wave owns a (BM/WAVES_M) x (BN/WAVES_N) block of the output tile and,
+// for every k-tile, issues its share of the ring stage's loads. Load and compute overlap through the ring: while stage s is
 // consumed, the loads for the k-tile STAGES-1 ahead are in flight. The
 // hand-off of a stage (producer commit -> consumer wait, consumer release ->
 // producer acquire, in the pages' acquire/commit/wait/release terms of the
