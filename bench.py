@@ -193,17 +193,22 @@ def tail_idle(pts, wl, ops, schedule, conc=None):
                 tiles_per_worker_min=int(per.min()), tiles_per_worker_max=int(per.max()))
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the HIP sources the GEMM kernel is built from."""
+def kernel_source_digest(base=None) -> str:
+    """sha256 over the HIP sources the GEMM kernel is built from, with comments
+    and blank space removed (a comment edit does not change the kernel)."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    base = os.path.join(ROOT, "persistent_tile_scheduling_amd", "csrc")
+    base = base or os.path.join(ROOT, "persistent_tile_scheduling_amd", "csrc")
     for dirpath, _, files in sorted(os.walk(base)):
         for f in sorted(files):
             if f.endswith((".h", ".hip")):
                 path = os.path.join(dirpath, f)
+                text = open(path, encoding="utf-8").read()
+                text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+                text = re.sub(r"//[^\n]*", " ", text)
                 h.update(os.path.relpath(path, base).encode())
-                h.update(open(path, "rb").read())
+                h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
