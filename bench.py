@@ -13,7 +13,9 @@ stream the kernel is launched on.
 Workloads (--workload): c2 (default) 8192^3 bf16 out 256x256 tiles; c1 256^3
 fp32 out 64x64 tiles; c3 5000x7000x3000 fp32 out; c4 64 grouped problems
 M_g in {128..4096}, N = K = 4096, bf16 out; c5 16384^2 x 8192 bf16 out beside a
-concurrent 2^30-element int16 copy on a second stream.
+concurrent 2^30-element int16 copy on a second stream limited to 64 compute
+units; c6 64 grouped problems 1024 x 1024 with per-problem K_g in
+{256..8192} (tiles of unequal cost), bf16 out.
 """
 from __future__ import annotations
 
@@ -47,6 +49,10 @@ def workload(name: str):
         ms = gen.grouped_m_draw(0)
         return dict(desc="grouped bf16 GEMM, 64 problems M_g~U{128..4096}, N=K=4096, bf16 out, one launch",
                     shapes=[(m, 4096, 4096) for m in ms], out=torch.bfloat16, tile=(256, 256), copy=0)
+    if name == "c6":
+        ks = gen.grouped_k_draw(0)
+        return dict(desc="grouped bf16 GEMM, 64 problems 1024x1024, K_g~U{256..8192}, bf16 out, one launch",
+                    shapes=[(1024, 1024, k) for k in ks], out=torch.bfloat16, tile=(256, 256), copy=0)
     if name == "c5":
         return dict(desc="bf16 GEMM 16384x16384x8192, bf16 out, beside a concurrent 2^30 int16 copy",
                     shapes=[(16384, 16384, 8192)], out=torch.bfloat16, tile=(256, 256), copy=1 << 30)
@@ -263,7 +269,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--schedules", default="static,dynamic,dynamic_xcd")
+    ap.add_argument("--schedules", default="static,dynamic,dynamic_xcd,nonpersistent")
     ap.add_argument("--tile-k", type=int, default=0, help="k-tile depth (0 = library default)")
     ap.add_argument("--stages", type=int, default=0, help="LDS ring stages (0 = library default)")
     ap.add_argument("--load-path", type=int, default=0, help="1 = global->LDS, 2 = via registers (0 = default)")

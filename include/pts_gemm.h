@@ -70,8 +70,17 @@ typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout;
 /* STATIC: grid-stride. DYNAMIC: every tile claimed from one device-wide
  * counter. DYNAMIC_XCD: one counter per XCD (chiplet) over a contiguous range
  * of tiles, so the tiles in flight on an XCD share its L2; a worker whose
- * XCD's range is used up claims from the other ranges in turn. */
-typedef enum { GEMM_SCHEDULE_STATIC = 0, GEMM_SCHEDULE_DYNAMIC = 1, GEMM_SCHEDULE_DYNAMIC_XCD = 2 } gemm_schedule;
+ * XCD's range is used up claims from the other ranges in turn.
+ * NONPERSISTENT: not a persistent kernel -- one workgroup per tile (grid =
+ * tile count), dispatched by the hardware as compute units free up; the
+ * comparison point the persistent schedules replace ("Schedules", section
+ * "Scheduling Shapes"). num_workers must be 0 with it. */
+typedef enum {
+    GEMM_SCHEDULE_STATIC = 0,
+    GEMM_SCHEDULE_DYNAMIC = 1,
+    GEMM_SCHEDULE_DYNAMIC_XCD = 2,
+    GEMM_SCHEDULE_NONPERSISTENT = 3
+} gemm_schedule;
 
 /* Largest group count one plan accepts: the per-problem operand pointers of a
  * run travel in the kernel's argument block. */
@@ -104,7 +113,7 @@ typedef struct {
     int32_t load_path;         /* how a ring stage is filled: 0 = default, 1 = global->LDS loads,
                                   2 = global->registers->LDS (256x256, tile_k 64, 2 stages) */
     int32_t waves;             /* waves per workgroup: 0 = default, 4 (one per SIMD) or 8 (two per
-                                  SIMD; 256x256, tile_k 64, 2 stages) */
+                                  SIMD; 256x256 with tile_k 64 and 2 stages or tile_k 32 and 4) */
     int32_t schedule;          /* gemm_schedule */
     int32_t num_workers;       /* 0 = one per compute unit times occupancy, capped at the tile count */
     uint32_t flags;            /* GEMM_FLAG_* */
@@ -154,7 +163,8 @@ gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream);
  * ensure no run of the plan is still executing. */
 gemm_status gemm_plan_destroy(gemm_plan *plan);
 
-/* Tile count, worker count (grid size) and LDS bytes per workgroup of a plan.
+/* Tile count, worker count (grid size; the tile count for the non-persistent
+ * schedule) and LDS bytes per workgroup of a plan.
  * Any output pointer may be NULL. */
 gemm_status gemm_plan_query(const gemm_plan *plan, int64_t *num_tiles, int32_t *num_workers,
                             int32_t *lds_bytes);
@@ -179,9 +189,13 @@ gemm_status gemm_plan_query(const gemm_plan *plan, int64_t *num_tiles, int32_t *
  */
 gemm_status gemm_plan_set_trace(gemm_plan *plan, void *device_buf, size_t bytes);
 
+/* Size of the scheduler's counter block: the plan's own, and the `counters`
+ * array that pts_sched_probe takes. */
+#define GEMM_SCHED_COUNTER_BYTES 36864
+
 /*
  * Read the plan's scheduler counters (synchronizes the device): out[0] the
- * live claim counter (0 between dynamic runs), out[1] the live exit counter
+ * live claim counters, summed (0 between dynamic runs), out[1] the live exit counter
  * (0 between runs), out[2] the total number of claims in the last dynamic run
  * (single counter: tiles + workers, since every worker's loop ends on exactly
  * one failed claim), out[3] the number of dynamic runs completed.
@@ -219,8 +233,9 @@ gemm_status pts_stream_destroy(void *stream);
  * (bounded by spin_limit polls; on expiry out_status[0] = 1), which replays a
  * worker that starts late. out_tiles holds the logical index (static) or
  * counter value (dynamic) of each tile, or its position (per-XCD claiming).
- * counters: device array of 16 uint32 zeroed by the caller before the first
- * call (the claim counters reset themselves at the end of every call).
+ * counters: device array of GEMM_SCHED_COUNTER_BYTES bytes, zeroed by the
+ * caller before the first call (the claim counters reset themselves at the
+ * end of every call); 4-byte aligned.
  * out_status: device array of 1 uint32.
  */
 gemm_status pts_sched_probe(int32_t num_tiles, int32_t num_workers, int32_t schedule,

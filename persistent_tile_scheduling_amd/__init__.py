@@ -32,6 +32,8 @@ GEMM_COL_MAJOR = 1
 GEMM_SCHEDULE_STATIC = 0
 GEMM_SCHEDULE_DYNAMIC = 1
 GEMM_SCHEDULE_DYNAMIC_XCD = 2
+GEMM_SCHEDULE_NONPERSISTENT = 3
+GEMM_SCHED_COUNTER_BYTES = 36864
 GEMM_MAX_GROUPS = 64
 GEMM_FLAG_NONE = 0
 
@@ -218,7 +220,8 @@ class Plan:
                  num_workers: int = 0):
         if isinstance(schedule, str):
             schedule = {"static": GEMM_SCHEDULE_STATIC, "dynamic": GEMM_SCHEDULE_DYNAMIC,
-                        "dynamic_xcd": GEMM_SCHEDULE_DYNAMIC_XCD}[schedule]
+                        "dynamic_xcd": GEMM_SCHEDULE_DYNAMIC_XCD,
+                        "nonpersistent": GEMM_SCHEDULE_NONPERSISTENT}[schedule]
         dtype_d = {torch.float32: GEMM_DTYPE_F32, torch.bfloat16: GEMM_DTYPE_BF16}[out_dtype]
         self.shapes = [tuple(s) for s in shapes]
         self.out_dtype = out_dtype

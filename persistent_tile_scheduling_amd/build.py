@@ -22,6 +22,10 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     # Packed fp32 instructions are kept out of the device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # The scheduler's claim is one lane's atomic whose result is read a tile
+    # later. The atomic optimizer would rewrite it into a wave-wide form that
+    # reads the result at once, i.e. waits for the round trip on the spot.
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

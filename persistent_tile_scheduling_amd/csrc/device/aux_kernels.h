@@ -34,7 +34,8 @@ __global__ __launch_bounds__(256) void copy_int16_kernel(const int4 *__restrict_
 // polls at most spin_limit times; on expiry status[0] = 1 and the worker goes
 // on, so the kernel always ends.
 //
-// counters: [0, CTR_WORDS) as in TileScheduler, [CTR_WORDS] workers done
+// counters: CTR_WORDS words laid out as in TileScheduler, with CTR_GATE
+// counting the workers that have finished
 // (gate), reset by the gated worker once it passes.
 __global__ __launch_bounds__(64) void sched_probe_kernel(int32_t num_tiles, int32_t num_workers, int32_t mode,
                                                          int32_t gate_worker, int64_t work_ticks,
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(64) void sched_probe_kernel(int32_t num_tiles, int3
 
     if (w == gate_worker) {
         int64_t polls = 0;
-        while (__hip_atomic_load(counters + CTR_WORDS, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <
+        while (__hip_atomic_load(counters + CTR_GATE, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <
                    (uint32_t)(num_workers - 1) &&
                polls < spin_limit) {
             __builtin_amdgcn_s_sleep(8);
@@ -57,10 +58,11 @@ __global__ __launch_bounds__(64) void sched_probe_kernel(int32_t num_tiles, int3
         if (polls >= spin_limit && leader)
             __hip_atomic_store(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (leader)
-            __hip_atomic_store(counters + CTR_WORDS, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(counters + CTR_GATE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    TileScheduler sched{counters, num_tiles, num_workers, w, mode, slots, (int)(xcc_id_reg() % NUM_XCD), 0u};
+    TileScheduler sched{counters, num_tiles, num_workers, num_workers, w, mode, slots,
+                        (int)(xcc_id_reg() % NUM_XCD), 0u};
     Claimed cur = sched.first(leader);
     int seq = 0;
     while (cur.pos < num_tiles) {
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(64) void sched_probe_kernel(int32_t num_tiles, int3
         out_counts[w] = seq;
     wait_all();
     if (leader && gate_worker >= 0 && w != gate_worker)
-        __hip_atomic_fetch_add(counters + CTR_WORDS, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(counters + CTR_GATE, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     sched.finish(leader);
 }
 

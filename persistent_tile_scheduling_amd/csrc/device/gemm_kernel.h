@@ -74,6 +74,8 @@ struct GemmArgs {
     int32_t total_tiles;
     int32_t num_workers;
     int32_t schedule;
+    int32_t round;     // static dealing width (see static_position)
+    int32_t pad;
     uint64_t d_vec_ok; // bit g: problem g's D rows allow vector stores
     const uint16_t *a[PTS_MAX_GROUPS];
     const uint16_t *b[PTS_MAX_GROUPS];
@@ -431,14 +433,19 @@ struct Mainloop {
         barrier_lds();
     }
 
-    __device__ __forceinline__ void run(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI])
+    // The tile's k loop. `on_last_stage` runs (in every wave) once the last
+    // k-tile's stage is ready and no further load of this tile is waited for
+    // with vmcnt, so a memory operation it issues overlaps the last k-tile's
+    // MFMAs and the epilogue without any load wait stalling on it.
+    template <class Hook>
+    __device__ __forceinline__ void run(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI], Hook &&on_last_stage)
     {
         if constexpr (C::LOAD_PATH == LOAD_REG)
-            run_regs(t, acc);
+            run_regs(t, acc, on_last_stage);
         else if constexpr (C::STAGES >= 3)
-            run_spread(t, acc);
+            run_spread(t, acc, on_last_stage);
         else
-            run_burst(t, acc);
+            run_burst(t, acc, on_last_stage);
     }
 
     // ---- register path ----------------------------------------------------
@@ -538,13 +545,16 @@ struct Mainloop {
     // stores. Past the last k-tile the loads re-read k-tile nk-1 and the
     // stores go to a stage that is not read again, which keeps the loop free
     // of branches.
-    __device__ __forceinline__ void run_regs(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI])
+    template <class Hook>
+    __device__ __forceinline__ void run_regs(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI], Hook &on_last_stage)
     {
         static_assert(C::STAGES == 2, "register path uses two LDS stages");
         static_assert(C::KSTEPS >= 3 && C::KSTEPS % 2 == 0 && C::LOADS % (C::KSTEPS / 2) == 0, "staging split");
         const int nk = t.nk;
-        if (nk == 0)
+        if (nk == 0) {
+            on_last_stage();
             return;
+        }
         const bool ktail = (t.k % C::BK) != 0;
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
@@ -576,23 +586,30 @@ struct Mainloop {
             }
             regs_kstep_ops<C::KSTEPS - 1>(f[(C::KSTEPS - 1) & 1], acc, stage, kt_load, t);
         }
+        // the staging loads run to the end of the loop
+        on_last_stage();
     }
 
     // ---- global->LDS path -------------------------------------------------
     // Two stages: the loads of k-tile kt+2 can only start once every wave has
     // left stage kt, i.e. at the barrier that ends k-tile kt; they are issued
     // there in one burst.
-    __device__ __forceinline__ void run_burst(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI])
+    template <class Hook>
+    __device__ __forceinline__ void run_burst(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI], Hook &on_last_stage)
     {
         const int nk = t.nk;
-        if (nk == 0)
+        if (nk == 0) {
+            on_last_stage();
             return;
+        }
         const int pro = min(C::STAGES - 1, nk);
         for (int s = 0; s < pro; ++s)
             issue_any(s, s, t.k, nk);
         stage_ready(0, t);
         if (C::STAGES - 1 < nk)
             issue_any(C::STAGES - 1, C::STAGES - 1, t.k, nk);
+        if (nk == 1)
+            on_last_stage();
         Frags f[2];
         load_frags(0, 0, f[0]);
         for (int kt = 0; kt < nk; ++kt) {
@@ -609,6 +626,8 @@ struct Mainloop {
                 stage_ready(kt + 1, t);
                 if (kt + C::STAGES < nk)
                     issue_any(kt + C::STAGES, stage, t.k, nk);
+                if (kt + 2 == nk)
+                    on_last_stage();
                 load_frags((kt + 1) % C::STAGES, 0, f[C::KSTEPS & 1]);
             }
             // one MFMA site for the last k-step keeps the accumulators in one
@@ -621,13 +640,16 @@ struct Mainloop {
     // barrier that ends kt, and k-tile kt+STAGES goes into it; its loads are
     // spread over the MFMAs of k-tile kt+1 (LOADS/KSTEPS per k-step), so they
     // land STAGES-2 k-tiles before they are read.
-    __device__ __forceinline__ void run_spread(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI])
+    template <class Hook>
+    __device__ __forceinline__ void run_spread(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI], Hook &on_last_stage)
     {
         static_assert(C::LOADS % C::KSTEPS == 0, "loads split evenly over k-steps");
         constexpr int PER_STEP = C::LOADS / C::KSTEPS;
         const int nk = t.nk;
-        if (nk == 0)
+        if (nk == 0) {
+            on_last_stage();
             return;
+        }
         const int pro = min(C::STAGES, nk);
         for (int s = 0; s < pro; ++s)
             issue_any(s, s, t.k, nk);
@@ -636,6 +658,8 @@ struct Mainloop {
         if ((t.k % C::BK) != 0 && nk == 1)
             zero_k_tail(0, 0, t.k);
         barrier_lds();
+        if (nk == 1)
+            on_last_stage();
         Frags f[2];
         load_frags(0, 0, f[0]);
         for (int kt = 0; kt < nk; ++kt) {
@@ -662,6 +686,8 @@ struct Mainloop {
                 if ((t.k % C::BK) != 0 && kt + 1 == nk - 1)
                     zero_k_tail(kt + 1, (kt + 1) % C::STAGES, t.k);
                 barrier_lds();
+                if (kt + 2 == nk)
+                    on_last_stage();
                 load_frags((kt + 1) % C::STAGES, 0, f[C::KSTEPS & 1]);
             }
             mma_with_loads<PER_STEP>(f[(C::KSTEPS - 1) & 1], acc, dma, (C::KSTEPS - 1) * PER_STEP, dma_kt, dma_stage,
@@ -803,8 +829,8 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     ml.wn = wave % C::WAVES_N;
     ml.setup_fragments();
 
-    TileScheduler sched{args->counters, args->total_tiles, args->num_workers, (int)blockIdx.x, args->schedule,
-                        sched_slots, (int)(xcc_id_reg() % NUM_XCD), 0u};
+    TileScheduler sched{args->counters, args->total_tiles, args->num_workers, args->round, (int)blockIdx.x,
+                        args->schedule, sched_slots, (int)(xcc_id_reg() % NUM_XCD), 0u};
     uint8_t *const trace = args->trace;
     const int total_tiles = args->total_tiles;
     const bool tracing = trace != nullptr;
@@ -814,7 +840,6 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     int seq = 0;
     while (cur.pos < total_tiles) {
         const uint64_t t_tile0 = tracing ? realtime() : 0;
-        sched.claim_ahead(leader);
         const TileCtx<C> tc = decode_tile<C>(args, cur.pos);
 
         f32x16 acc[C::MI][C::NI];
@@ -825,7 +850,10 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
                 acc[mi][ni] = f32x16{};
 
         ml.setup(tc);
-        ml.run(tc, acc);
+        // The request for the next tile goes out once this tile's last stage
+        // is in LDS: its round trip overlaps the last k-tile and the epilogue,
+        // and no load wait of this tile is held up by it.
+        ml.run(tc, acc, [&] { sched.claim_ahead(leader); });
         // every wave has finished reading the ring before it is reused for staging
         barrier_raw();
         store_epilogue<C>(tc, acc, ml.wm, ml.wn, lane, tid, smem);

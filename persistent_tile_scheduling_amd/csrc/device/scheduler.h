@@ -45,21 +45,32 @@
 // claims from its own XCD's range and, once that is used up, from the other
 // ranges in turn (work stealing across XCDs); its loop ends only when every
 // range is used up. Every position is still handed out exactly once.
+//
+// Non-persistent comparison point: one workgroup per tile (grid = T), which
+// the hardware dispatches as compute units free up; each workgroup runs one
+// tile and exits ("Schedules", section "Scheduling Shapes": the one-tile-per-
+// CTA shape the persistent loop replaces).
 #pragma once
 
 #include "common.h"
 
 namespace pts {
 
-enum : int { SCHED_STATIC = 0, SCHED_DYNAMIC = 1, SCHED_DYNAMIC_XCD = 2 };
+enum : int { SCHED_STATIC = 0, SCHED_DYNAMIC = 1, SCHED_DYNAMIC_XCD = 2, SCHED_NONPERSISTENT = 3 };
 
 constexpr int NUM_XCD = 8;           // chiplets (XCDs) of an MI355X, each with its own L2
+// Counter words. Counters that are hit at the same time sit in separate 4 KiB
+// blocks, so their atomics are spread over memory channels instead of queueing
+// at one.
 constexpr int CTR_CLAIM = 0;         // single device-wide claim counter
-constexpr int CTR_EXIT = 1;          // workers that have made their final claim
-constexpr int CTR_FINAL = 2;         // total claims of the last dynamic run
-constexpr int CTR_RUNS = 3;          // dynamic runs completed
-constexpr int CTR_XCD = 4;           // [4, 12): per-XCD claim counters
-constexpr int CTR_WORDS = CTR_XCD + NUM_XCD;
+constexpr int CTR_EXIT = 32;         // workers that have made their final claim
+constexpr int CTR_FINAL = 64;        // total claims of the last dynamic run
+constexpr int CTR_RUNS = 65;         // dynamic runs completed
+constexpr int CTR_GATE = 96;         // scheduler probe: workers finished (late-worker gate)
+constexpr int CTR_XCD_STRIDE = 1024; // per-XCD claim counter x at CTR_XCD_STRIDE * (x + 1)
+constexpr int CTR_WORDS = CTR_XCD_STRIDE * (NUM_XCD + 1);
+
+__host__ __device__ constexpr int ctr_xcd(int x) { return CTR_XCD_STRIDE * (x + 1); }
 
 // Tiles are numbered along a locality-friendly order ("positions", see
 // tile_position below); a scheduler hands out positions. Split [0, n) into
@@ -76,9 +87,12 @@ __device__ __forceinline__ int part_begin(int n, int parts, int p)
 // This bijection of each round onto itself gives those workers consecutive
 // positions, i.e. one compact block of the output per XCD and round, whose
 // A and B panels that XCD's L2 then shares. It only permutes which tile a
-// logical index denotes; every position is still used exactly once.
-__device__ __forceinline__ int static_position(int t, int num_tiles, int num_workers)
+// logical index denotes; every position is still used exactly once. (The
+// non-persistent schedule uses the same dealing with P = the number of
+// workgroups resident at once.)
+__device__ __forceinline__ int static_position(int t, int num_tiles, int round)
 {
+    const int num_workers = round;
     const int base = (t / num_workers) * num_workers;
     const int r = min(num_workers, num_tiles - base);
     const int u = t - base;
@@ -99,6 +113,7 @@ struct TileScheduler {
     uint32_t *counters;
     int32_t num_tiles;
     int32_t num_workers;
+    int32_t round;    // static dealing width: P (static) or resident workgroups (non-persistent)
     int32_t worker;
     int32_t mode;
     int32_t *slots;   // four LDS words: two (claim, pos) pairs, alternating by tile parity
@@ -114,7 +129,7 @@ struct TileScheduler {
     // or on this XCD's counter. Its value is read only in resolve().
     __device__ __forceinline__ void issue()
     {
-        pending = atomic_take(mode == SCHED_DYNAMIC ? CTR_CLAIM : CTR_XCD + xcd);
+        pending = atomic_take(mode == SCHED_DYNAMIC ? CTR_CLAIM : ctr_xcd(xcd));
     }
 
     // Turn the request into a tile (leader lane only). Single counter: the
@@ -133,7 +148,7 @@ struct TileScheduler {
             const int x = (xcd + d) % NUM_XCD;
             const int lo = part_begin(num_tiles, NUM_XCD, x), hi = part_begin(num_tiles, NUM_XCD, x + 1);
             if (d > 0)
-                v = atomic_take(CTR_XCD + x);
+                v = atomic_take(ctr_xcd(x));
             if (v < (uint32_t)(hi - lo))
                 return Claimed{(int32_t)(x * 0x1000000 + v), lo + (int32_t)v};
         }
@@ -154,9 +169,9 @@ struct TileScheduler {
     // First tile of this worker; all threads of the workgroup call it.
     __device__ __forceinline__ Claimed first(bool leader)
     {
-        if (mode == SCHED_STATIC) {
+        if (mode == SCHED_STATIC || mode == SCHED_NONPERSISTENT) {
             const int32_t t = worker;
-            return Claimed{t, t < num_tiles ? static_position(t, num_tiles, num_workers) : num_tiles};
+            return Claimed{t, t < num_tiles ? static_position(t, num_tiles, round) : num_tiles};
         }
         if (leader)
             issue();
@@ -164,9 +179,11 @@ struct TileScheduler {
     }
 
     // Issue the request for the tile after the current one (leader only).
+    __device__ __forceinline__ bool claims() const { return mode == SCHED_DYNAMIC || mode == SCHED_DYNAMIC_XCD; }
+
     __device__ __forceinline__ void claim_ahead(bool leader)
     {
-        if (mode != SCHED_STATIC && leader)
+        if (claims() && leader)
             issue();
     }
 
@@ -177,21 +194,23 @@ struct TileScheduler {
     {
         if (mode == SCHED_STATIC) {
             const int32_t t = current.claim + num_workers;
-            return Claimed{t, t < num_tiles ? static_position(t, num_tiles, num_workers) : num_tiles};
+            return Claimed{t, t < num_tiles ? static_position(t, num_tiles, round) : num_tiles};
         }
+        if (mode == SCHED_NONPERSISTENT)
+            return Claimed{0x7FFFFFFF, num_tiles}; // one tile per workgroup
         return publish_and_read(leader, (seq + 1) & 1);
     }
 
     // End-of-kernel bookkeeping (leader only; after the worker's failed claim).
     __device__ __forceinline__ void finish(bool leader)
     {
-        if (mode == SCHED_STATIC || !leader)
+        if (!claims() || !leader)
             return;
         uint32_t old = __hip_atomic_fetch_add(counters + CTR_EXIT, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         if (old == (uint32_t)num_workers - 1u) {
             uint32_t total = __hip_atomic_exchange(counters + CTR_CLAIM, 0u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
             for (int x = 0; x < NUM_XCD; ++x)
-                total += __hip_atomic_exchange(counters + CTR_XCD + x, 0u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                total += __hip_atomic_exchange(counters + ctr_xcd(x), 0u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(counters + CTR_FINAL, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_fetch_add(counters + CTR_RUNS, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(counters + CTR_EXIT, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);

@@ -65,6 +65,8 @@ const std::vector<KernelEntry> &kernel_table()
         make_entry<256, 256, 64, 2, false, pts::LOAD_DMA, 2, 4>(),
         make_entry<256, 256, 64, 2, true, pts::LOAD_REG, 2, 4>(),
         make_entry<256, 256, 64, 2, false, pts::LOAD_REG, 2, 4>(),
+        make_entry<256, 256, 32, 4, true, pts::LOAD_DMA, 2, 4>(),
+        make_entry<256, 256, 32, 4, false, pts::LOAD_DMA, 2, 4>(),
         make_entry<256, 256, 64, 2, true>(),  make_entry<256, 256, 64, 2, false>(),
         make_entry<256, 256, 32, 4, true>(),  make_entry<256, 256, 32, 4, false>(),
         make_entry<256, 256, 64, 2, true, pts::LOAD_REG>(), make_entry<256, 256, 64, 2, false, pts::LOAD_REG>(),
@@ -85,6 +87,7 @@ struct gemm_plan {
     std::vector<gemm_shape> shapes; // ld values resolved
     int32_t dtype_d = GEMM_DTYPE_F32;
     int32_t schedule = GEMM_SCHEDULE_STATIC;
+    int32_t round = 0;
     KernelEntry kernel{};
     int64_t total_tiles = 0;
     int32_t workers = 0;
@@ -131,9 +134,11 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
         return fail(GEMM_ERR_UNSUPPORTED, "A and B must be bf16 and the accumulator fp32");
     if (desc->dtype_d != GEMM_DTYPE_F32 && desc->dtype_d != GEMM_DTYPE_BF16)
         return fail(GEMM_ERR_UNSUPPORTED, "D must be fp32 or bf16");
-    if (desc->schedule != GEMM_SCHEDULE_STATIC && desc->schedule != GEMM_SCHEDULE_DYNAMIC &&
-        desc->schedule != GEMM_SCHEDULE_DYNAMIC_XCD)
-        return fail(GEMM_ERR_INVALID_VALUE, "schedule must be static (0), dynamic (1) or dynamic per XCD (2)");
+    if (desc->schedule < GEMM_SCHEDULE_STATIC || desc->schedule > GEMM_SCHEDULE_NONPERSISTENT)
+        return fail(GEMM_ERR_INVALID_VALUE,
+                    "schedule must be static (0), dynamic (1), dynamic per XCD (2) or non-persistent (3)");
+    if (desc->schedule == GEMM_SCHEDULE_NONPERSISTENT && desc->num_workers > 0)
+        return fail(GEMM_ERR_INVALID_VALUE, "the non-persistent schedule launches one workgroup per tile");
     if (desc->num_workers < 0)
         return fail(GEMM_ERR_INVALID_VALUE, "num_workers must be >= 0");
     if (desc->flags != GEMM_FLAG_NONE)
@@ -225,9 +230,15 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
         return e != hipSuccess ? hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor")
                                : fail(GEMM_ERR_UNSUPPORTED, "kernel cannot be resident on this device");
     }
-    int64_t workers = desc->num_workers > 0 ? desc->num_workers : std::min<int64_t>(tiles, (int64_t)cus * occ);
+    const int64_t resident = (int64_t)cus * occ;
+    int64_t workers = desc->num_workers > 0 ? desc->num_workers : std::min<int64_t>(tiles, resident);
+    int64_t round = workers;
+    if (desc->schedule == GEMM_SCHEDULE_NONPERSISTENT) {
+        workers = tiles;
+        round = std::min<int64_t>(tiles, resident);
+    }
     if (tiles == 0)
-        workers = 0;
+        workers = round = 0;
     if (workers > 65535 * 16) {
         delete plan;
         return fail(GEMM_ERR_INVALID_VALUE, "num_workers too large");
@@ -239,20 +250,24 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
     plan->kernel = *entry;
     plan->total_tiles = tiles;
     plan->workers = (int32_t)workers;
+    plan->round = (int32_t)round;
 
+    // counters first (4 KiB aligned blocks), then the group table
+    const size_t cbytes = sizeof(uint32_t) * pts::CTR_WORDS;
+    static_assert(sizeof(uint32_t) * pts::CTR_WORDS == GEMM_SCHED_COUNTER_BYTES, "counter block size");
     const size_t gbytes = sizeof(pts::GroupDesc) * groups.size();
     void *mem = nullptr;
-    e = hipMalloc(&mem, gbytes + 128);
+    e = hipMalloc(&mem, cbytes + gbytes);
     if (e != hipSuccess) {
         delete plan;
         (void)hipGetLastError();
-        return fail(GEMM_ERR_OUT_OF_MEMORY, "hipMalloc of %zu bytes failed", gbytes + 128);
+        return fail(GEMM_ERR_OUT_OF_MEMORY, "hipMalloc of %zu bytes failed", cbytes + gbytes);
     }
-    plan->d_groups = (pts::GroupDesc *)mem;
-    plan->d_counters = (uint32_t *)((uint8_t *)mem + gbytes);
+    plan->d_counters = (uint32_t *)mem;
+    plan->d_groups = (pts::GroupDesc *)((uint8_t *)mem + cbytes);
     e = hipMemcpy(plan->d_groups, groups.data(), gbytes, hipMemcpyHostToDevice);
     if (e == hipSuccess)
-        e = hipMemset(plan->d_counters, 0, 128);
+        e = hipMemset(plan->d_counters, 0, cbytes);
     if (e == hipSuccess)
         e = hipDeviceSynchronize();
     if (e != hipSuccess) {
@@ -309,9 +324,24 @@ gemm_status gemm_plan_read_counters(const gemm_plan *plan, uint32_t out[4])
     if (plan == nullptr || out == nullptr)
         return fail(GEMM_ERR_INVALID_VALUE, "plan or out is NULL");
     hipError_t e = hipDeviceSynchronize();
+    uint32_t words[pts::CTR_RUNS + 1];
     if (e == hipSuccess)
-        e = hipMemcpy(out, plan->d_counters, 4 * sizeof(uint32_t), hipMemcpyDeviceToHost);
-    return e == hipSuccess ? GEMM_OK : hip_fail(e, "reading counters");
+        e = hipMemcpy(words, plan->d_counters, sizeof(words), hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return hip_fail(e, "reading counters");
+    uint32_t live_xcd = 0;
+    for (int x = 0; x < pts::NUM_XCD && e == hipSuccess; ++x) {
+        uint32_t v = 0;
+        e = hipMemcpy(&v, plan->d_counters + pts::ctr_xcd(x), sizeof(v), hipMemcpyDeviceToHost);
+        live_xcd += v;
+    }
+    if (e != hipSuccess)
+        return hip_fail(e, "reading counters");
+    out[0] = words[pts::CTR_CLAIM] + live_xcd;
+    out[1] = words[pts::CTR_EXIT];
+    out[2] = words[pts::CTR_FINAL];
+    out[3] = words[pts::CTR_RUNS];
+    return GEMM_OK;
 }
 
 gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream)
@@ -358,6 +388,7 @@ gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream)
     args.total_tiles = (int32_t)plan->total_tiles;
     args.num_workers = plan->workers;
     args.schedule = plan->schedule;
+    args.round = plan->round;
 
     void *kargs[] = {&args};
     e = hipLaunchKernel(plan->kernel.fn, dim3(plan->workers), dim3(plan->kernel.waves * 64), kargs, 0,

@@ -38,6 +38,7 @@ _MASK64 = (1 << 64) - 1
 TENSOR_A = 1
 TENSOR_B = 2
 TENSOR_M_DRAW = 3
+TENSOR_K_DRAW = 4
 TENSOR_COPY_SRC = 5
 
 _CHUNK = 1 << 22
@@ -172,6 +173,17 @@ def grouped_m_draw(seed: int, groups: int = 64, step: int = 128, levels: int = 3
     With the defaults this draws each M_g uniformly from {128, 256, ..., 4096}.
     """
     x = stream_u64(seed, TENSOR_M_DRAW, groups)
+    u24 = (x >> np.uint64(40)).astype(np.int64)
+    return [int(step * (1 + (int(v) * levels >> 24))) for v in u24]
+
+
+def grouped_k_draw(seed: int, groups: int = 64, step: int = 256, levels: int = 32) -> list[int]:
+    """Per-problem depths ``K_g = step * (1 + floor(levels * u_g))`` from tensor id 4.
+
+    With the defaults this draws each K_g uniformly from {256, 512, ..., 8192}:
+    a grouped GEMM whose tiles cost in proportion to their problem's K.
+    """
+    x = stream_u64(seed, TENSOR_K_DRAW, groups)
     u24 = (x >> np.uint64(40)).astype(np.int64)
     return [int(step * (1 + (int(v) * levels >> 24))) for v in u24]
 

@@ -52,7 +52,9 @@ def test_status_strings(binding):
     (dict(layouts=(1, 1, 0)), 2, "layouts"),
     (dict(dtypes=(1, 0, 1)), 2, "bf16"),
     (dict(dtype_d=7), 2, "fp32 or bf16"),
-    (dict(schedule=3), 1, "schedule"),
+    (dict(schedule=4), 1, "schedule"),
+    (dict(schedule=-1), 1, "schedule"),
+    (dict(schedule=3, num_workers=2), 1, "one workgroup per tile"),
     (dict(num_workers=-1), 1, "num_workers"),
     (dict(flags=0x80), 2, "flags"),
     (dict(tile=(96, 96)), 2, "not built"),
@@ -114,3 +116,15 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(d, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "oracle_gemm" not in text, f
+
+
+def test_header_constants_match_the_binding(binding):
+    import re
+    text = open(os.path.join(ROOT, "include", "pts_gemm.h")).read()
+    defines = dict(re.findall(r"#define (GEMM_[A-Z_]+) (\d+)", text))
+    assert defines, "no numeric constants found in the header"
+    for name, value in defines.items():
+        assert getattr(binding, name) == int(value), name
+    enums = dict(re.findall(r"(GEMM_SCHEDULE_[A-Z_]+) = (\d+)", text))
+    for name, value in enums.items():
+        assert getattr(binding, name) == int(value), name

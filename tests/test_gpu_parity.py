@@ -7,8 +7,8 @@ Bars (the tolerance is written here, per case):
   1e-2 sqrt(K) (bf16 output), over every element at oracle-sized shapes and
   over sampled entries (every tile's four corners plus random entries) at the
   full configuration sizes;
-* static, dynamic and per-XCD dynamic schedules -- bitwise identical D
-  (same tile body).
+* static, dynamic, per-XCD dynamic and non-persistent schedules -- bitwise
+  identical D (same tile body).
 """
 from __future__ import annotations
 
@@ -22,7 +22,8 @@ from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
 
-SCHEDULES = ("static", "dynamic", "dynamic_xcd")
+SCHEDULES = ("static", "dynamic", "dynamic_xcd", "nonpersistent")
+PERSISTENT = SCHEDULES[:3]   # the schedules that take a worker count
 
 
 @pytest.fixture(scope="module")
@@ -75,7 +76,8 @@ SWEEP = [(1, 1, 1), (7, 7, 7), (63, 65, 64), (64, 64, 64), (65, 63, 65), (127, 1
 
 # every built kernel: (tile_m, tile_n, tile_k, stages)
 KERNELS = [(64, 64, 64, 2, 1, 4), (128, 128, 64, 2, 1, 4), (128, 128, 32, 4, 1, 4), (256, 256, 64, 2, 1, 4),
-           (256, 256, 32, 4, 1, 4), (256, 256, 64, 2, 2, 4), (256, 256, 64, 2, 2, 8), (256, 256, 64, 2, 1, 8)]
+           (256, 256, 32, 4, 1, 4), (256, 256, 64, 2, 2, 4), (256, 256, 64, 2, 2, 8), (256, 256, 64, 2, 1, 8),
+           (256, 256, 32, 4, 1, 8)]
 
 
 @pytest.mark.parametrize("tile", KERNELS)
@@ -100,7 +102,7 @@ def test_integer_exact_sweep(pts, tile, out_dtype):
                                    (40, 3000, 100)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("tile", [(256, 256, 64, 2, 1, 4), (256, 256, 32, 4, 1, 4), (256, 256, 64, 2, 2, 4),
-                                  (256, 256, 64, 2, 2, 8), (256, 256, 64, 2, 1, 8)])
+                                  (256, 256, 64, 2, 2, 8), (256, 256, 64, 2, 1, 8), (256, 256, 32, 4, 1, 8)])
 def test_random_ragged_full_oracle(pts, shape, out_dtype, tile):
     m, n, k = shape
     lda, ldb, ldd = _padded_ld(k) + 16, _padded_ld(k) + 8, n + 5
@@ -172,7 +174,7 @@ def test_tile_reuse_does_not_accumulate_across_tiles(pts):
     a_bits, b_bits = _operands(m, n, k, 13, kind="integer")
     ref = oracle.gemm(a_bits, b_bits, m, n, k)
     a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
-    for sched in SCHEDULES:
+    for sched in PERSISTENT:
         d, _, (tiles, workers) = U.run_single(m, n, k, a, b, torch.float32, sched, tile=(128, 128), num_workers=1)
         assert (tiles, workers) == (16, 1)
         U.check_exact(d, ref, f"single worker {sched}")
@@ -183,7 +185,7 @@ def test_more_workers_than_tiles(pts):
     a_bits, b_bits = _operands(m, n, k, 2, kind="integer")
     ref = oracle.gemm(a_bits, b_bits, m, n, k)
     a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
-    for sched in SCHEDULES:
+    for sched in PERSISTENT:
         d, counters, (tiles, workers) = U.run_single(m, n, k, a, b, torch.float32, sched, tile=(64, 64),
                                                      num_workers=9)
         assert (tiles, workers) == (4, 9)
@@ -221,6 +223,38 @@ def test_grouped_small_full_oracle(pts):
     for sched in SCHEDULES[1:]:
         for x, y in zip(outs["static"], outs[sched]):
             assert torch.equal(x.nan_to_num(0.0), y.nan_to_num(0.0))
+
+
+def test_grouped_variable_k_full_oracle(pts):
+    # per-problem K (tiles of unequal cost), ragged M, N and K, fp32 out
+    rng = np.random.default_rng(6)
+    shapes = [(int(rng.integers(1, 400)), int(rng.integers(1, 400)), int(rng.integers(1, 40)) * 8 + int(rng.integers(0, 8)))
+              for _ in range(9)] + [(300, 200, 0), (257, 129, 1)]
+    tensors, refs = [], []
+    for g, (m, n, k) in enumerate(shapes):
+        ta, tb = gen.group_tensor_ids(g)
+        ld = _padded_ld(k)
+        a_bits = gen.operand_a(m, k, 2, tensor_id=ta, lda=ld)
+        b_bits = gen.operand_b(k, n, 2, tensor_id=tb, ldb=ld)
+        refs.append(oracle.gemm(a_bits, b_bits, m, n, k, lda=ld, ldb=ld))
+        tensors.append((U.bits_to_device(a_bits), U.bits_to_device(b_bits),
+                        torch.full((m, n), float("nan"), dtype=torch.float32, device=U.DEV)))
+    plan_shapes = [(m, n, k, _padded_ld(k), _padded_ld(k), 0) for (m, n, k) in shapes]
+    outs = {}
+    for sched in SCHEDULES:
+        U.log(f"grouped variable K {sched}")
+        for (_, _, d) in tensors:
+            d.fill_(float("nan"))
+        with pts.Plan(plan_shapes, torch.float32, schedule=sched) as p:
+            p.run(tensors)
+            torch.cuda.synchronize()
+            U.check_counters(sched, p.counters(), p.num_tiles, p.num_workers)
+        for g, ((m, n, k), (_, _, d)) in enumerate(zip(shapes, tensors)):
+            U.check_close(d, refs[g], max(k, 1), f"group {g} {(m, n, k)} {sched}")
+        outs[sched] = [d.clone() for (_, _, d) in tensors]
+    for sched in SCHEDULES[1:]:
+        for x, y in zip(outs["static"], outs[sched]):
+            assert torch.equal(x, y)
 
 
 # ---------------------------------------------------------------------------
@@ -282,6 +316,37 @@ def test_config4_grouped_64_problems_sampled(pts):
         worst = 0.0
         for g, ((rows, cols), ref) in enumerate(zip(samples, refs)):
             worst = max(worst, U.check_sampled(tensors[g][2], rows, cols, ref, k, f"config4 group {g} {sched}"))
+        U.log(f"  sampled max err {worst:.3g}")
+        outs[sched] = [t[2].clone() for t in tensors]
+    for sched in SCHEDULES[1:]:
+        for x, y in zip(outs["static"], outs[sched]):
+            assert torch.equal(x, y)
+
+
+def test_config6_grouped_variable_k_sampled(pts):
+    seed, m, n = 0, 1024, 1024
+    ks = gen.grouped_k_draw(seed)
+    shapes = [(m, n, k) for k in ks]
+    tensors = []
+    for g, k in enumerate(ks):
+        ta, tb = gen.group_tensor_ids(g)
+        tensors.append((U.device_uniform(m, k, seed, ta), U.device_uniform(n, k, seed, tb),
+                        torch.empty((m, n), dtype=torch.bfloat16, device=U.DEV)))
+    samples = U.sample_entries([(m, n)] * len(ks), 256, 256, 32, seed=3)
+    refs = []
+    for g, ((rows, cols), k) in enumerate(zip(samples, ks)):
+        ta, tb = gen.group_tensor_ids(g)
+        refs.append(U.oracle_sampled(seed, ta, tb, k, rows, cols))
+    outs = {}
+    for sched in SCHEDULES:
+        U.log(f"config6 grouped variable K {sched} sum(K)={sum(ks)}")
+        with pts.Plan(shapes, torch.bfloat16, schedule=sched) as p:
+            p.run(tensors)
+            torch.cuda.synchronize()
+            U.check_counters(sched, p.counters(), p.num_tiles, p.num_workers)
+        worst = 0.0
+        for g, ((rows, cols), ref, k) in enumerate(zip(samples, refs, ks)):
+            worst = max(worst, U.check_sampled(tensors[g][2], rows, cols, ref, k, f"config6 group {g} {sched}"))
         U.log(f"  sampled max err {worst:.3g}")
         outs[sched] = [t[2].clone() for t in tensors]
     for sched in SCHEDULES[1:]:

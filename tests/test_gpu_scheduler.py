@@ -51,7 +51,7 @@ def _probe(pts, tiles, workers, schedule, gate=-1, work_ns=20000, maxpw=None, co
     out = torch.full((workers, maxpw), -1, dtype=torch.int32, device=U.DEV)
     counts = torch.full((workers,), -1, dtype=torch.int32, device=U.DEV)
     if counters is None:
-        counters = torch.zeros(16, dtype=torch.int32, device=U.DEV)
+        counters = torch.zeros(pts.GEMM_SCHED_COUNTER_BYTES // 4, dtype=torch.int32, device=U.DEV)
     status = torch.zeros(1, dtype=torch.int32, device=U.DEV)
     pts.pts_sched_probe(tiles, workers, schedule, gate, work_ns, 2_000_000, out, counts, maxpw, counters, status)
     torch.cuda.synchronize()
@@ -59,7 +59,13 @@ def _probe(pts, tiles, workers, schedule, gate=-1, work_ns=20000, maxpw=None, co
     cnt = counts.cpu().tolist()
     rows = out.cpu().tolist()
     per_worker = [rows[w][:cnt[w]] for w in range(workers)]
-    return per_worker, counters.cpu().tolist()
+    return per_worker, _counter_summary(counters)
+
+
+def _counter_summary(counters):
+    """[claim, exit, final claim total, runs] followed by the 8 per-XCD counters."""
+    c = counters.cpu().tolist()
+    return [c[0], c[32], c[64], c[65]] + [c[1024 * (x + 1)] for x in range(8)]
 
 
 def test_probe_static_matches_printed_example(pts, golden_dir):
@@ -89,7 +95,7 @@ def test_probe_dynamic_late_worker_finds_nothing(pts):
 
 def test_probe_dynamic_at_scale_and_repeated(pts):
     # one counter block across runs: each run must leave it reset for the next
-    shared = torch.zeros(16, dtype=torch.int32, device=U.DEV)
+    shared = torch.zeros(pts.GEMM_SCHED_COUNTER_BYTES // 4, dtype=torch.int32, device=U.DEV)
     for run in range(3):
         per_worker, counters = _probe(pts, 4096, 256, pts.GEMM_SCHEDULE_DYNAMIC, work_ns=2000, counters=shared)
         oracle.check_dynamic_claims(per_worker, 4096)
@@ -154,7 +160,7 @@ def _traced_run(pts, shapes, schedule, tile=(0, 0), num_workers=0, out_dtype=tor
         return tiles.copy(), workers.copy(), p.num_tiles, p.num_workers, p.counters()
 
 
-@pytest.mark.parametrize("schedule", ["static", "dynamic", "dynamic_xcd"])
+@pytest.mark.parametrize("schedule", ["static", "dynamic", "dynamic_xcd", "nonpersistent"])
 @pytest.mark.parametrize("shapes,tile", [([(5000, 7000)], (256, 256)), ([(256, 256)], (64, 64)),
                                          ([(300, 200), (0, 10), (1000, 64), (1, 1)], (128, 128)),
                                          ([(20000, 2048)], (256, 256))])
@@ -179,6 +185,8 @@ def test_gemm_trace_covers_every_tile_once(pts, schedule, shapes, tile):
     assert np.all(tiles["xcc_id"] == workers["xcc_id"][tiles["worker"]])
     if schedule == "static":
         assert per_worker == oracle.static_assignment(nt, nw)
+    elif schedule == "nonpersistent":
+        assert nw == nt and per_worker == [[w] for w in range(nw)]
     elif schedule == "dynamic":
         assert np.array_equal(tiles["claim"], tiles["tile"])
         oracle.check_dynamic_claims(per_worker, nt)

@@ -74,6 +74,15 @@ def test_grouped_m_draw():
     assert len(set(ms)) > 16
 
 
+def test_grouped_k_draw():
+    ks = gen.grouped_k_draw(0)
+    assert len(ks) == 64
+    assert all(k % 256 == 0 and 256 <= k <= 8192 for k in ks)
+    assert gen.grouped_k_draw(0) == ks
+    assert len(set(ks)) > 16
+    assert ks != gen.grouped_m_draw(0, step=256)   # its own tensor id, not the M draw's
+
+
 def test_operand_layouts_and_padding():
     a = gen.operand_a(4, 6, 0, lda=16)
     assert a.shape == (4, 16)
