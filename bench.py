@@ -195,8 +195,34 @@ def tail_idle(pts, wl, ops, schedule, conc=None):
     idle = float(((end.max() - end).sum()) / (len(end) * span)) if span > 0 else 0.0
     late = float(((start - start.min()).sum()) / (len(end) * span)) if span > 0 else 0.0
     per = workers["tiles"]
+    busy_ns = (tiles["t_end"] - tiles["t_start"]).astype("float64").sum() * 10.0
+    clock = float(tiles["cycles"].astype("float64").sum() / busy_ns) if busy_ns > 0 else None
     return dict(tail_idle_frac=idle, late_start_frac=late, span_us=span / 100.0,
-                tiles_per_worker_min=int(per.min()), tiles_per_worker_max=int(per.max()))
+                tiles_per_worker_min=int(per.min()), tiles_per_worker_max=int(per.max()),
+                clock_ghz=clock)
+
+
+def vendor_gemm(wl, ops, steps):
+    """Context only: the vendor BLAS (torch.mm -> hipBLASLt) on the same single
+    problem and operands, D = A . B with B given as its (n x k) transpose."""
+    import torch
+    (m, n, k), = wl["shapes"]
+    a, b, _ = ops[0]
+    out = torch.empty((m, n), dtype=wl["out"], device="cuda")
+    if wl["out"] != torch.bfloat16:
+        return None
+    bt = b.t()
+    for _ in range(5):
+        torch.mm(a, bt, out=out)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        torch.mm(a, bt, out=out)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    return dict(kernel_ms_avg=ms, tflops=2.0 * m * n * k / (ms * 1e-3) / 1e12, library="torch.mm (hipBLASLt)")
 
 
 def kernel_source_digest(base=None) -> str:
@@ -266,8 +292,8 @@ def cpu_baseline(wl, budget_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--schedules", default="static,dynamic,dynamic_xcd,nonpersistent")
     ap.add_argument("--tile-k", type=int, default=0, help="k-tile depth (0 = library default)")
@@ -279,6 +305,8 @@ def main():
     ap.add_argument("--no-trace", action="store_true")
     ap.add_argument("--compare-rounds", type=int, default=10,
                     help="interleaved rounds of every schedule for the comparison (0 = skip)")
+    ap.add_argument("--no-vendor", dest="vendor", action="store_false",
+                    help="skip the vendor BLAS context timing")
     ap.add_argument("--copy-cus", type=int, default=64,
                     help="compute units the concurrent copy may use (0 = all, unmasked stream)")
     ap.add_argument("--calibration-copy", type=int, default=0,
@@ -331,6 +359,9 @@ def main():
                   file=sys.stderr, flush=True)
     if conc is not None:
         conc.close()
+    vendor = vendor_gemm(wl, ops, args.steps) if args.vendor and len(wl["shapes"]) == 1 else None
+    if vendor:
+        print(f"# vendor {vendor['library']}: {vendor['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     line = {
         "metric": METRIC,
@@ -358,6 +389,15 @@ def main():
         "schedules": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in results.items()},
     }
+    clock = results.get(head_sched, {}).get("clock_ghz")
+    if clock:
+        # the same launch against the MFMA peak at the clock the chip actually held
+        peak_at_clock = 256 * 4096 * clock * 1e9 / 1e12
+        line["roofline"]["clock_ghz_measured"] = round(clock, 3)
+        line["roofline"]["peak_at_measured_clock"] = round(peak_at_clock, 1)
+        line["roofline"]["frac_at_measured_clock"] = round(head["kernel_tflops"] / peak_at_clock, 4)
+    if vendor:
+        line["vendor_library"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in vendor.items()}
     if "static" in results and "kernel_ms_median" in results["static"]:
         line["dynamic_vs_static"] = {s: round(results["static"]["kernel_ms_median"] / r["kernel_ms_median"], 4)
                                      for s, r in results.items() if s != "static" and "kernel_ms_median" in r}

@@ -173,8 +173,8 @@ gemm_status gemm_plan_query(const gemm_plan *plan, int64_t *num_tiles, int32_t *
  * Per-tile trace (test and benchmark use). After this call every run writes,
  * into `device_buf`, one record per tile followed by one record per worker:
  *
- *   struct { int32 tile, claim, worker, seq, group, row0, col0; uint32 xcc_id;
- *            uint64 t_start, t_end; }              -- 48 bytes, at index `tile`
+ *   struct { int32 tile, claim, worker, seq, group, row0, col0; uint32 xcc_id,
+ *            cycles, pad; uint64 t_start, t_end; } -- 56 bytes, at index `tile`
  *   struct { uint64 t_start, t_end; int32 tiles, worker; uint32 hw_id, xcc_id; }
  *                                                  -- 32 bytes, at index `worker`
  *
@@ -184,7 +184,9 @@ gemm_status gemm_plan_query(const gemm_plan *plan, int64_t *num_tiles, int32_t *
  * index; dynamic: the counter value; per-XCD: XCD * 2^24 + counter value).
  * Times are the 100 MHz device real-time counter; seq is the tile's place in
  * its worker's sequence; hw_id is the wave's HW_ID register and xcc_id its
- * XCC (chiplet) id. `bytes` must be >= 48 * num_tiles + 32 * num_workers.
+ * XCC (chiplet) id; `cycles` counts shader-clock cycles over the same span,
+ * so cycles / (10 ns * (t_end - t_start)) is the clock in GHz.
+ * `bytes` must be >= 56 * num_tiles + 32 * num_workers.
  * device_buf = NULL switches tracing off.
  */
 gemm_status gemm_plan_set_trace(gemm_plan *plan, void *device_buf, size_t bytes);

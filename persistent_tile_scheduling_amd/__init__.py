@@ -37,7 +37,7 @@ GEMM_SCHED_COUNTER_BYTES = 36864
 GEMM_MAX_GROUPS = 64
 GEMM_FLAG_NONE = 0
 
-TILE_TRACE_BYTES = 48
+TILE_TRACE_BYTES = 56
 WORKER_TRACE_BYTES = 32
 
 
@@ -265,8 +265,8 @@ def decode_trace(buf: torch.Tensor, num_tiles: int, num_workers: int):
     import numpy as np
     raw = buf.detach().cpu().contiguous().view(torch.uint8).numpy()
     tile_dt = np.dtype([("tile", "<i4"), ("claim", "<i4"), ("worker", "<i4"), ("seq", "<i4"), ("group", "<i4"),
-                        ("row0", "<i4"), ("col0", "<i4"), ("xcc_id", "<u4"), ("t_start", "<u8"),
-                        ("t_end", "<u8")])
+                        ("row0", "<i4"), ("col0", "<i4"), ("xcc_id", "<u4"), ("cycles", "<u4"), ("pad", "<u4"),
+                        ("t_start", "<u8"), ("t_end", "<u8")])
     worker_dt = np.dtype([("t_start", "<u8"), ("t_end", "<u8"), ("tiles", "<i4"), ("worker", "<i4"),
                           ("hw_id", "<u4"), ("xcc_id", "<u4")])
     nt = TILE_TRACE_BYTES * num_tiles

@@ -110,6 +110,9 @@ __device__ __forceinline__ uint32_t hw_id_reg()
     return v;
 }
 
+// Shader (core) clock counter; with realtime() it gives the clock frequency.
+__device__ __forceinline__ uint64_t shader_cycles() { return __builtin_amdgcn_s_memtime(); }
+
 __device__ __forceinline__ uint32_t xcc_id_reg()
 {
     uint32_t v;

@@ -55,9 +55,11 @@ struct GroupDesc {
 struct TileTrace {
     int32_t tile, claim, worker, seq, group, row0, col0;
     uint32_t xcc_id;
+    uint32_t cycles; // shader-clock cycles from t_start to t_end (clock = cycles / elapsed)
+    uint32_t pad;
     uint64_t t_start, t_end;
 };
-static_assert(sizeof(TileTrace) == 48, "trace record layout");
+static_assert(sizeof(TileTrace) == 56, "trace record layout");
 
 struct WorkerTrace {
     uint64_t t_start, t_end;
@@ -739,9 +741,12 @@ struct Epilogue {
     static_assert(LDS_BYTES <= 150 * 1024, "epilogue staging must fit LDS");
 };
 
-template <class C>
+// `on_staged` runs once, after the first pass's accumulators are written to
+// LDS and before the barrier that publishes them, so an LDS write it makes is
+// visible to every wave after that barrier.
+template <class C, class Hook>
 __device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const f32x16 (&acc)[C::MI][C::NI],
-                                               int wm, int wn, int lane, int tid, uint8_t *smem)
+                                               int wm, int wn, int lane, int tid, uint8_t *smem, Hook &&on_staged)
 {
     using E = Epilogue<C>;
     const int lr = lane & 31, lc = (lane >> 5) * 4;
@@ -765,6 +770,8 @@ __device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const f32x16
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        if (pass == 0)
+            on_staged();
         barrier_lds();
         // LDS -> D, one 4-element group per lane per step
         constexpr int TOTAL = E::PASS_ROWS * E::CHUNKS_ROW;
@@ -840,6 +847,7 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     int seq = 0;
     while (cur.pos < total_tiles) {
         const uint64_t t_tile0 = tracing ? realtime() : 0;
+        const uint64_t c_tile0 = tracing ? shader_cycles() : 0;
         const TileCtx<C> tc = decode_tile<C>(args, cur.pos);
 
         f32x16 acc[C::MI][C::NI];
@@ -856,7 +864,10 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
         ml.run(tc, acc, [&] { sched.claim_ahead(leader); });
         // every wave has finished reading the ring before it is reused for staging
         barrier_raw();
-        store_epilogue<C>(tc, acc, ml.wm, ml.wn, lane, tid, smem);
+        // The next tile's claim is resolved while the accumulators are staged
+        // (its request went out a k-tile ago) and published by the staging
+        // barrier, so no wave waits on it after the stores.
+        store_epilogue<C>(tc, acc, ml.wm, ml.wn, lane, tid, smem, [&] { sched.stage_next(leader, seq); });
 
         if (tracing && leader) {
             TileTrace r;
@@ -870,13 +881,17 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
             r.xcc_id = xcc_id_reg();
             r.t_start = t_tile0;
             r.t_end = realtime();
+            r.cycles = (uint32_t)(shader_cycles() - c_tile0);
+            r.pad = 0;
             ((TileTrace *)trace)[cur.pos] = r;
         }
-        // Stores and loads may retire out of order with respect to each other,
-        // so the next tile's load accounting starts from an empty counter.
-        wait_all();
+        // The D stores stay in flight into the next tile's prologue (the first
+        // stage wait covers them: loads complete in issue order and an older
+        // store only makes a vmcnt wait stricter). Staging reads must be done
+        // in every wave before the next tile's loads overwrite the ring.
+        wait_lgkmcnt0();
         barrier_raw();
-        cur = sched.next(cur, leader, seq);
+        cur = sched.read_next(cur, seq);
         ++seq;
     }
 

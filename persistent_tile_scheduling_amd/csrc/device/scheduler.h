@@ -192,13 +192,39 @@ struct TileScheduler {
     // `seq` is the current tile's position in this worker's sequence.
     __device__ __forceinline__ Claimed next(Claimed current, bool leader, int seq)
     {
+        if (!claims())
+            return next_computed(current);
+        return publish_and_read(leader, (seq + 1) & 1);
+    }
+
+    // The same in two halves, for a caller that already has barriers to use:
+    // stage_next (leader; dynamic modes resolve the pending claim and write
+    // it to LDS), then, after at least one LDS barrier, read_next (all).
+    __device__ __forceinline__ void stage_next(bool leader, int seq)
+    {
+        if (claims() && leader) {
+            const Claimed c = resolve();
+            const int slot = (seq + 1) & 1;
+            slots[2 * slot] = c.claim;
+            slots[2 * slot + 1] = c.pos;
+        }
+    }
+
+    __device__ __forceinline__ Claimed read_next(Claimed current, int seq)
+    {
+        if (!claims())
+            return next_computed(current);
+        const int slot = (seq + 1) & 1;
+        return Claimed{uniform(slots[2 * slot]), uniform(slots[2 * slot + 1])};
+    }
+
+    __device__ __forceinline__ Claimed next_computed(Claimed current) const
+    {
         if (mode == SCHED_STATIC) {
             const int32_t t = current.claim + num_workers;
             return Claimed{t, t < num_tiles ? static_position(t, num_tiles, round) : num_tiles};
         }
-        if (mode == SCHED_NONPERSISTENT)
-            return Claimed{0x7FFFFFFF, num_tiles}; // one tile per workgroup
-        return publish_and_read(leader, (seq + 1) & 1);
+        return Claimed{0x7FFFFFFF, num_tiles}; // non-persistent: one tile per workgroup
     }
 
     // End-of-kernel bookkeeping (leader only; after the worker's failed claim).

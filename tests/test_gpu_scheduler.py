@@ -182,6 +182,10 @@ def test_gemm_trace_covers_every_tile_once(pts, schedule, shapes, tile):
         assert seqs == list(range(len(p)))
     assert workers["worker"].tolist() == list(range(nw))
     assert np.all(tiles["t_end"] >= tiles["t_start"])
+    span_ns = (tiles["t_end"] - tiles["t_start"]).astype(np.float64).sum() * 10.0
+    if span_ns > 0:
+        clock = tiles["cycles"].astype(np.float64).sum() / span_ns
+        assert 0.3 < clock < 3.0, f"implausible shader clock {clock:.3f} GHz"
     assert np.all(tiles["xcc_id"] == workers["xcc_id"][tiles["worker"]])
     if schedule == "static":
         assert per_worker == oracle.static_assignment(nt, nw)
