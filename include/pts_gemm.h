@@ -114,6 +114,8 @@ typedef struct {
                                   2 = global->registers->LDS (256x256, tile_k 64, 2 stages) */
     int32_t waves;             /* waves per workgroup: 0 = default, 4 (one per SIMD) or 8 (two per
                                   SIMD; 256x256 with tile_k 64 and 2 stages or tile_k 32 and 4) */
+    int32_t mfma;              /* matrix instruction: 0 = default, 32 (32x32x16) or 16 (16x16x32;
+                                  256x256, 8 waves, global->LDS loads) */
     int32_t schedule;          /* gemm_schedule */
     int32_t num_workers;       /* 0 = one per compute unit times occupancy, capped at the tile count */
     uint32_t flags;            /* GEMM_FLAG_* */

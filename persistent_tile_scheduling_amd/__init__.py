@@ -52,7 +52,7 @@ class GemmDesc(ctypes.Structure):
                 ("dtype_a", ctypes.c_int32), ("dtype_b", ctypes.c_int32), ("dtype_acc", ctypes.c_int32),
                 ("dtype_d", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("tile_k", ctypes.c_int32), ("stages", ctypes.c_int32), ("load_path", ctypes.c_int32),
-                ("waves", ctypes.c_int32),
+                ("waves", ctypes.c_int32), ("mfma", ctypes.c_int32),
                 ("schedule", ctypes.c_int32), ("num_workers", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
@@ -131,20 +131,20 @@ def gemm_last_error() -> str:
     return _lib.gemm_last_error().decode()
 
 
-def make_desc(shapes, dtype_d: int = GEMM_DTYPE_F32, tile=(0, 0, 0, 0, 0, 0), schedule: int = GEMM_SCHEDULE_STATIC,
+def make_desc(shapes, dtype_d: int = GEMM_DTYPE_F32, tile=(0, 0, 0, 0, 0, 0, 0), schedule: int = GEMM_SCHEDULE_STATIC,
               num_workers: int = 0, flags: int = GEMM_FLAG_NONE, layouts=(GEMM_ROW_MAJOR, GEMM_COL_MAJOR,
                                                                            GEMM_ROW_MAJOR),
               dtypes=(GEMM_DTYPE_BF16, GEMM_DTYPE_BF16, GEMM_DTYPE_F32)):
     """Build a ``gemm_desc``. ``shapes`` is a list of (m, n, k[, lda, ldb, ldd]);
-    ``tile`` is (tile_m, tile_n[, tile_k, stages, load_path, waves]) with 0 for defaults."""
+    ``tile`` is (tile_m, tile_n[, tile_k, stages, load_path, waves, mfma]) with 0 for defaults."""
     arr = (GemmShape * max(1, len(shapes)))()
     for i, s in enumerate(shapes):
         s = tuple(s) + (0,) * (6 - len(s))
         arr[i] = GemmShape(*[int(v) for v in s])
-    tile = tuple(tile) + (0,) * (6 - len(tile))
+    tile = tuple(tile) + (0,) * (7 - len(tile))
     d = GemmDesc(len(shapes), ctypes.cast(arr, ctypes.POINTER(GemmShape)), layouts[0], layouts[1], layouts[2],
                  dtypes[0], dtypes[1], dtypes[2], dtype_d, tile[0], tile[1], tile[2], tile[3], tile[4], tile[5],
-                 schedule, num_workers, flags)
+                 tile[6], schedule, num_workers, flags)
     d._shapes_keepalive = arr
     return d
 

@@ -6,7 +6,8 @@
 // accumulator, which the store writes to D):
 //
 //   HBM --(128-bit global->LDS loads)--> LDS ring of STAGES stages (A and B)
-//       --(ds_read_b128 fragments)--> v_mfma_f32_32x32x16_bf16, fp32 in AGPRs
+//       --(ds_read_b128 fragments)--> v_mfma_f32_32x32x16_bf16 or
+//           v_mfma_f32_16x16x32_bf16, fp32 accumulators in registers
 //       --(masked epilogue, fp32 or bf16 round-to-nearest-even)--> D
 //
 // Workgroup: WAVES_M x WAVES_N waves (2 x 2, or 2 x 4 for two waves per SIMD);
@@ -90,12 +91,35 @@ enum : int {
     LOAD_REG = 1  // global -> registers one k-tile ahead, then ds_write
 };
 
+// The matrix instruction: a 32x32 output block per 16-deep k-step, or a 16x16
+// block per 32-deep k-step. Both take one 16-byte fragment per lane for each
+// operand (8 consecutive k of one row of A / column of B) and do the same
+// work per cycle; the 16x16 form needs two waves per SIMD to issue at full
+// rate and draws less power per operation, so it holds a higher clock.
+template <int MB> struct Mfma;
+template <> struct Mfma<32> {
+    using Acc = f32x16;
+    static constexpr int KM = 16;
+    static __device__ __forceinline__ Acc run(bf16x8 x, bf16x8 y, Acc c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<16> {
+    using Acc = f32x4;
+    static constexpr int KM = 32;
+    static __device__ __forceinline__ Acc run(bf16x8 x, bf16x8 y, Acc c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
+    }
+};
+
 // WAVES_M x WAVES_N waves per workgroup, one wave tile each. 2 x 2 gives one
 // wave per SIMD (512 registers each); 2 x 4 gives two waves per SIMD (256
 // registers each), so one wave's LDS and memory waits overlap the other's
-// MFMAs.
+// MFMAs. MB is the matrix instruction's output block edge (32 or 16).
 template <int BM_, int BN_, int BK_, int STAGES_, bool OUT_BF16_, int LOAD_PATH_ = LOAD_DMA, int WAVES_M_ = 2,
-          int WAVES_N_ = 2>
+          int WAVES_N_ = 2, int MB_ = 32>
 struct GemmConfig {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
     static constexpr bool OUT_BF16 = OUT_BF16_;
@@ -103,8 +127,12 @@ struct GemmConfig {
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
     static constexpr int WAVES_PER_SIMD = WAVES / 4;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N; // wave tile
-    static constexpr int MI = WTM / 32, NI = WTN / 32;           // 32x32 MFMA blocks per wave
-    static constexpr int KSTEPS = BK / 16;                       // MFMA k-steps per k-tile
+    static constexpr int MB = MB_;                               // MFMA output block edge
+    using Op = Mfma<MB>;
+    using Acc = typename Op::Acc;                                // one block's accumulators per lane
+    static constexpr int MI = WTM / MB, NI = WTN / MB;           // MFMA blocks per wave
+    static constexpr int KSTEPS = BK / Op::KM;                   // MFMA k-steps per k-tile
+    static constexpr int KCHUNKS = Op::KM / 8;                   // 16-byte chunks per row per k-step
     static constexpr int ROW_BYTES = BK * 2;                     // one row of A (column of B) per k-tile
     static constexpr int CHUNKS = BK / 8;                        // 16-byte chunks per row
     static constexpr int A_BYTES = BM * ROW_BYTES, B_BYTES = BN * ROW_BYTES;
@@ -115,7 +143,7 @@ struct GemmConfig {
     static constexpr int LOADS = A_LOADS + B_LOADS;
     static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
     static_assert(BK == 32 || BK == 64, "k-tile");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+    static_assert(WTM % MB == 0 && WTN % MB == 0 && KSTEPS >= 1, "wave tile");
     static_assert(A_LOADS >= 1 && B_LOADS >= 1 && A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0,
                   "stage must split into whole 1 KiB wave loads");
     static_assert(STAGES >= 2 && (STAGES - 2) * LOADS <= 63, "vmcnt range");
@@ -338,16 +366,17 @@ struct Mainloop {
             zero_chunk_tail(sb + (wave * C::B_LOADS + i) * 1024 + lane * 16, koff + load_chunk(i, C::B_LOADS) * 8, k);
     }
 
-    // Byte offset, inside a 32-row block, of this lane's fragment for k-step
-    // ks: row lane%32, logical chunk 2*ks + lane/32.
+    // Byte offset, inside an MB-row block, of this lane's fragment for k-step
+    // ks: row lane%MB, logical chunk KCHUNKS*ks + lane/MB.
     uint32_t frag_off[C::KSTEPS];
 
     __device__ __forceinline__ void setup_fragments()
     {
-        const int lr = lane & 31, lk = lane >> 5;
+        const int lr = lane % C::MB, lk = lane / C::MB;
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks)
-            frag_off[ks] = (uint32_t)(lr * C::ROW_BYTES + (((2 * ks + lk) ^ lds_swizzle<C::BK>(lr)) << 4));
+            frag_off[ks] =
+                (uint32_t)(lr * C::ROW_BYTES + (((C::KCHUNKS * ks + lk) ^ lds_swizzle<C::BK>(lr)) << 4));
     }
 
     struct Frags {
@@ -363,29 +392,29 @@ struct Mainloop {
         const uint8_t *sb = smem + sbase + C::A_BYTES + wn * C::WTN * C::ROW_BYTES;
 #pragma unroll
         for (int mi = 0; mi < C::MI; ++mi)
-            f.a[mi] = *(const bf16x8 *)(sa + frag_off[ks] + mi * 32 * C::ROW_BYTES);
+            f.a[mi] = *(const bf16x8 *)(sa + frag_off[ks] + mi * C::MB * C::ROW_BYTES);
 #pragma unroll
         for (int ni = 0; ni < C::NI; ++ni)
-            f.b[ni] = *(const bf16x8 *)(sb + frag_off[ks] + ni * 32 * C::ROW_BYTES);
+            f.b[ni] = *(const bf16x8 *)(sb + frag_off[ks] + ni * C::MB * C::ROW_BYTES);
     }
 
     // MI x NI MFMAs of one k-step. The B fragment is the MFMA's first
-    // operand: the 32x32 result block is D^T, so each lane ends up holding 4
-    // consecutive columns of one row (what the epilogue wants).
-    static __device__ __forceinline__ void mma(const Frags &f, f32x16 (&acc)[C::MI][C::NI])
+    // operand: the result block is D^T, so each lane ends up holding groups of
+    // 4 consecutive columns of one row (what the epilogue wants).
+    static __device__ __forceinline__ void mma(const Frags &f, typename C::Acc (&acc)[C::MI][C::NI])
     {
 #pragma unroll
         for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
+                acc[mi][ni] = C::Op::run(f.b[ni], f.a[mi], acc[mi][ni]);
     }
 
     // The MFMAs of one k-step with loads [first, first + count) of k-tile
     // dma_kt issued between them, one load after every MFMAS/count MFMAs, so
     // the load instructions never stall the MFMA stream in one burst.
     template <int COUNT>
-    __device__ __forceinline__ void mma_with_loads(const Frags &f, f32x16 (&acc)[C::MI][C::NI], bool dma, int first,
+    __device__ __forceinline__ void mma_with_loads(const Frags &f, typename C::Acc (&acc)[C::MI][C::NI], bool dma, int first,
                                                    int dma_kt, int dma_stage, const TileCtx<C> &t)
     {
         constexpr int MFMAS = C::MI * C::NI;
@@ -394,7 +423,7 @@ struct Mainloop {
 #pragma unroll
         for (int x = 0; x < MFMAS; ++x) {
             const int mi = x / C::NI, ni = x % C::NI;
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
+            acc[mi][ni] = C::Op::run(f.b[ni], f.a[mi], acc[mi][ni]);
             if (x % EVERY == 0 && x / EVERY < COUNT && dma) {
                 const int i = first + x / EVERY;
                 if (tail)
@@ -440,14 +469,116 @@ struct Mainloop {
     // with vmcnt, so a memory operation it issues overlaps the last k-tile's
     // MFMAs and the epilogue without any load wait stalling on it.
     template <class Hook>
-    __device__ __forceinline__ void run(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI], Hook &&on_last_stage)
+    __device__ __forceinline__ void run(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI], Hook &&on_last_stage)
     {
         if constexpr (C::LOAD_PATH == LOAD_REG)
             run_regs(t, acc, on_last_stage);
         else if constexpr (C::STAGES >= 3)
             run_spread(t, acc, on_last_stage);
+        else if constexpr (C::MB == 16)
+            run_burst_rolling(t, acc, on_last_stage);
         else
             run_burst(t, acc, on_last_stage);
+    }
+
+    // ---- rolling fragments (16x16 blocks) ----------------------------------
+    // A 16x16 k-step needs MI + NI fragments; two whole sets do not fit two
+    // waves per SIMD. Instead the A fragments roll: after row mi's NI MFMAs,
+    // A[mi] is dead and its registers receive A[mi] of the next k-step; the B
+    // fragments of the next k-step go to a second B set, read during the
+    // first NI rows. One A set and two B sets are live.
+    struct RollFrags {
+        bf16x8 a[C::MI];
+        bf16x8 b[2][C::NI];
+    };
+
+    __device__ __forceinline__ const uint8_t *a_base(int stage) const
+    {
+        return smem + opaque_s((uint32_t)(stage * C::STAGE_BYTES)) + wm * C::WTM * C::ROW_BYTES;
+    }
+    __device__ __forceinline__ const uint8_t *b_base(int stage) const
+    {
+        return smem + opaque_s((uint32_t)(stage * C::STAGE_BYTES)) + C::A_BYTES + wn * C::WTN * C::ROW_BYTES;
+    }
+
+    __device__ __forceinline__ void read_all(int stage, int ks, RollFrags &f, int bset) const
+    {
+        const uint8_t *sa = a_base(stage), *sb = b_base(stage);
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi)
+            f.a[mi] = *(const bf16x8 *)(sa + frag_off[ks] + mi * C::MB * C::ROW_BYTES);
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni)
+            f.b[bset][ni] = *(const bf16x8 *)(sb + frag_off[ks] + ni * C::MB * C::ROW_BYTES);
+    }
+
+    // One k-step from (f.a, f.b[BS]) while reading k-step (stage, ks) into
+    // f.a (rolling) and f.b[BS ^ 1].
+    template <int BS>
+    __device__ __forceinline__ void rolling_step(RollFrags &f, typename C::Acc (&acc)[C::MI][C::NI], int stage,
+                                                 int ks) const
+    {
+        static_assert(C::NI <= C::MI, "B reads ride on the first NI rows");
+        const uint8_t *sa = a_base(stage), *sb = b_base(stage);
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi) {
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+                acc[mi][ni] = C::Op::run(f.b[BS][ni], f.a[mi], acc[mi][ni]);
+            f.a[mi] = *(const bf16x8 *)(sa + frag_off[ks] + mi * C::MB * C::ROW_BYTES);
+            if (mi < C::NI)
+                f.b[BS ^ 1][mi] = *(const bf16x8 *)(sb + frag_off[ks] + mi * C::MB * C::ROW_BYTES);
+        }
+#pragma unroll
+        for (int mi = 0; mi < C::NI; ++mi) {
+            __builtin_amdgcn_sched_group_barrier(0x008, C::NI, 0); // the row's MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // its A and B reads
+        }
+#pragma unroll
+        for (int mi = C::NI; mi < C::MI; ++mi) {
+            __builtin_amdgcn_sched_group_barrier(0x008, C::NI, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    }
+
+    template <class Hook>
+    __device__ __forceinline__ void run_burst_rolling(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI],
+                                                      Hook &on_last_stage)
+    {
+        static_assert(C::KSTEPS % 2 == 0, "B sets alternate by k-step parity");
+        const int nk = t.nk;
+        if (nk == 0) {
+            on_last_stage();
+            return;
+        }
+        issue_any(0, 0, t.k, nk);
+        stage_ready(0, t);
+        if (1 < nk)
+            issue_any(1, 1, t.k, nk);
+        if (nk == 1)
+            on_last_stage();
+        RollFrags f;
+        read_all(0, 0, f, 0);
+        for (int kt = 0; kt < nk; ++kt) {
+            const int stage = kt & 1;
+#pragma unroll
+            for (int ks = 0; ks + 1 < C::KSTEPS; ++ks) {
+                if (ks & 1)
+                    rolling_step<1>(f, acc, stage, ks + 1);
+                else
+                    rolling_step<0>(f, acc, stage, ks + 1);
+            }
+            if (kt + 1 < nk) {
+                stage_ready(kt + 1, t);
+                if (kt + 2 < nk)
+                    issue_any(kt + 2, stage, t.k, nk);
+                if (kt + 2 == nk)
+                    on_last_stage();
+            }
+            // The last k-step reads k-step 0 of the next k-tile's stage (past
+            // the last k-tile: a stage nobody writes any more; unused).
+            rolling_step<(C::KSTEPS - 1) & 1>(f, acc, stage ^ 1, 0);
+        }
     }
 
     // ---- register path ----------------------------------------------------
@@ -495,7 +626,7 @@ struct Mainloop {
     // registers receive chunk i of k-tile `kt` (ordered by the data
     // dependency), so every chunk spends one whole k-tile in flight.
     template <int COUNT>
-    __device__ __forceinline__ void mma_with_staging(const Frags &f, f32x16 (&acc)[C::MI][C::NI], int first,
+    __device__ __forceinline__ void mma_with_staging(const Frags &f, typename C::Acc (&acc)[C::MI][C::NI], int first,
                                                      int stage, int kt, const TileCtx<C> &t)
     {
         constexpr int MFMAS = C::MI * C::NI;
@@ -503,7 +634,7 @@ struct Mainloop {
 #pragma unroll
         for (int x = 0; x < MFMAS; ++x) {
             const int mi = x / C::NI, ni = x % C::NI;
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
+            acc[mi][ni] = C::Op::run(f.b[ni], f.a[mi], acc[mi][ni]);
             if (x % EVERY == 0 && x / EVERY < COUNT) {
                 const int i = first + x / EVERY;
                 swrite_one(i, stage);
@@ -513,7 +644,7 @@ struct Mainloop {
     }
 
     template <int KS>
-    __device__ __forceinline__ void regs_kstep_ops(const Frags &f, f32x16 (&acc)[C::MI][C::NI], int stage, int kt_load,
+    __device__ __forceinline__ void regs_kstep_ops(const Frags &f, typename C::Acc (&acc)[C::MI][C::NI], int stage, int kt_load,
                                                    const TileCtx<C> &t)
     {
         // staging happens in the k-steps [FIRST, KSTEPS-2]: all of them before
@@ -528,7 +659,7 @@ struct Mainloop {
     }
 
     template <int KS>
-    __device__ __forceinline__ void regs_steps(Frags (&f)[2], f32x16 (&acc)[C::MI][C::NI], int stage, int kt_load,
+    __device__ __forceinline__ void regs_steps(Frags (&f)[2], typename C::Acc (&acc)[C::MI][C::NI], int stage, int kt_load,
                                                const TileCtx<C> &t)
     {
         if constexpr (KS + 1 < C::KSTEPS) {
@@ -548,7 +679,7 @@ struct Mainloop {
     // stores go to a stage that is not read again, which keeps the loop free
     // of branches.
     template <class Hook>
-    __device__ __forceinline__ void run_regs(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI], Hook &on_last_stage)
+    __device__ __forceinline__ void run_regs(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI], Hook &on_last_stage)
     {
         static_assert(C::STAGES == 2, "register path uses two LDS stages");
         static_assert(C::KSTEPS >= 3 && C::KSTEPS % 2 == 0 && C::LOADS % (C::KSTEPS / 2) == 0, "staging split");
@@ -597,7 +728,7 @@ struct Mainloop {
     // left stage kt, i.e. at the barrier that ends k-tile kt; they are issued
     // there in one burst.
     template <class Hook>
-    __device__ __forceinline__ void run_burst(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI], Hook &on_last_stage)
+    __device__ __forceinline__ void run_burst(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI], Hook &on_last_stage)
     {
         const int nk = t.nk;
         if (nk == 0) {
@@ -643,7 +774,7 @@ struct Mainloop {
     // spread over the MFMAs of k-tile kt+1 (LOADS/KSTEPS per k-step), so they
     // land STAGES-2 k-tiles before they are read.
     template <class Hook>
-    __device__ __forceinline__ void run_spread(const TileCtx<C> &t, f32x16 (&acc)[C::MI][C::NI], Hook &on_last_stage)
+    __device__ __forceinline__ void run_spread(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI], Hook &on_last_stage)
     {
         static_assert(C::LOADS % C::KSTEPS == 0, "loads split evenly over k-steps");
         constexpr int PER_STEP = C::LOADS / C::KSTEPS;
@@ -715,14 +846,15 @@ struct Mainloop {
 
 // Epilogue: accumulators -> LDS -> D.
 //
-// With the B fragment as the MFMA's first operand, lane l of 32x32 block
-// (mi, ni) holds, for q = 0..3, the four consecutive columns 8q + 4(l/32) .. +3
-// of row l%32 in acc[4q .. 4q+3]. Each wave writes those 4-element groups
+// With the B fragment as the MFMA's first operand, lane l of an MB x MB block
+// (mi, ni) holds, for q = 0 .. MB/8 - 1, the four consecutive columns
+// 8q + 4(l/MB) .. +3 of row l%MB in acc[4q .. 4q+3] (32x32: q = 0..3; 16x16:
+// q = 0 only, l/16 = 0..3). Each wave writes those 4-element groups
 // as fp32 into a row-major staging tile in LDS (the ring is idle once the k
 // loop has ended; LDS stores take the accumulator registers directly); then
 // the workgroup stores the tile row by row, 4 elements per lane, converting
 // to bf16 there when D is bf16, so each wave writes whole contiguous row
-// segments of D. Rows are padded by 16 bytes so the 32 rows a wave writes in
+// segments of D. Rows are padded by 16 bytes so the rows a wave writes in
 // one instruction fall in distinct LDS banks.
 // Only rows < M and columns < N of the problem are written ("Schedules" page,
 // section "Domains": an index is stored only while it is in range).
@@ -745,11 +877,12 @@ struct Epilogue {
 // LDS and before the barrier that publishes them, so an LDS write it makes is
 // visible to every wave after that barrier.
 template <class C, class Hook>
-__device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const f32x16 (&acc)[C::MI][C::NI],
+__device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const typename C::Acc (&acc)[C::MI][C::NI],
                                                int wm, int wn, int lane, int tid, uint8_t *smem, Hook &&on_staged)
 {
     using E = Epilogue<C>;
-    const int lr = lane & 31, lc = (lane >> 5) * 4;
+    const int lr = lane % C::MB, lc = (lane / C::MB) * 4;
+    constexpr int QS = C::MB / 8; // 4-element groups per lane per block
     uint8_t *const tile_base = (uint8_t *)t.d + ((int64_t)t.row0 * t.ldd + t.col0) * E::ES;
 #pragma unroll
     for (int pass = 0; pass < E::PASSES; ++pass) {
@@ -757,12 +890,12 @@ __device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const f32x16
 #pragma unroll
         for (int m = 0; m < E::MI_PASS; ++m) {
             const int mi = pass * E::MI_PASS + m;
-            const int sr = wm * E::WAVE_ROWS + m * 32 + lr;
+            const int sr = wm * E::WAVE_ROWS + m * C::MB + lr;
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int c = wn * C::WTN + ni * 32 + 8 * q + lc;
+                for (int q = 0; q < QS; ++q) {
+                    const int c = wn * C::WTN + ni * C::MB + 8 * q + lc;
                     *(f32x4 *)(smem + sr * E::PITCH + c * 4) =
                         f32x4{acc[mi][ni][4 * q + 0], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
                               acc[mi][ni][4 * q + 3]};
@@ -850,12 +983,12 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
         const uint64_t c_tile0 = tracing ? shader_cycles() : 0;
         const TileCtx<C> tc = decode_tile<C>(args, cur.pos);
 
-        f32x16 acc[C::MI][C::NI];
+        typename C::Acc acc[C::MI][C::NI];
 #pragma unroll
         for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni)
-                acc[mi][ni] = f32x16{};
+                acc[mi][ni] = typename C::Acc{};
 
         ml.setup(tc);
         // The request for the next tile goes out once this tile's last stage

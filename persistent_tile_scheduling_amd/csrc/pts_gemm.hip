@@ -42,15 +42,16 @@ struct KernelEntry {
     bool out_bf16;
     int load_path;
     int waves;
+    int mfma;
     const void *fn;
     int lds_bytes;
 };
 
-template <int BM, int BN, int BK, int S, bool BF16, int LP = pts::LOAD_DMA, int WM = 2, int WN = 2>
+template <int BM, int BN, int BK, int S, bool BF16, int LP = pts::LOAD_DMA, int WM = 2, int WN = 2, int MB = 32>
 KernelEntry make_entry()
 {
-    using C = pts::GemmConfig<BM, BN, BK, S, BF16, LP, WM, WN>;
-    return KernelEntry{BM, BN, BK, S, BF16, LP, C::WAVES, (const void *)&pts::gemm_persistent_kernel<C>,
+    using C = pts::GemmConfig<BM, BN, BK, S, BF16, LP, WM, WN, MB>;
+    return KernelEntry{BM, BN, BK, S, BF16, LP, C::WAVES, MB, (const void *)&pts::gemm_persistent_kernel<C>,
                        C::LDS_BYTES};
 }
 
@@ -67,6 +68,8 @@ const std::vector<KernelEntry> &kernel_table()
         make_entry<256, 256, 64, 2, false, pts::LOAD_REG, 2, 4>(),
         make_entry<256, 256, 32, 4, true, pts::LOAD_DMA, 2, 4>(),
         make_entry<256, 256, 32, 4, false, pts::LOAD_DMA, 2, 4>(),
+        make_entry<256, 256, 64, 2, true, pts::LOAD_DMA, 2, 4, 16>(),
+        make_entry<256, 256, 64, 2, false, pts::LOAD_DMA, 2, 4, 16>(),
         make_entry<256, 256, 64, 2, true>(),  make_entry<256, 256, 64, 2, false>(),
         make_entry<256, 256, 32, 4, true>(),  make_entry<256, 256, 32, 4, false>(),
         make_entry<256, 256, 64, 2, true, pts::LOAD_REG>(), make_entry<256, 256, 64, 2, false, pts::LOAD_REG>(),
@@ -148,19 +151,21 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
     const bool out_bf16 = desc->dtype_d == GEMM_DTYPE_BF16;
     const KernelEntry *entry = nullptr;
     if (desc->tile_k < 0 || desc->stages < 0 || desc->load_path < 0 || desc->load_path > 2 ||
-        (desc->waves != 0 && desc->waves != 4 && desc->waves != 8))
-        return fail(GEMM_ERR_INVALID_VALUE, "tile_k and stages must be >= 0, load_path in 0..2, waves 0, 4 or 8");
+        (desc->waves != 0 && desc->waves != 4 && desc->waves != 8) ||
+        (desc->mfma != 0 && desc->mfma != 16 && desc->mfma != 32))
+        return fail(GEMM_ERR_INVALID_VALUE,
+                    "tile_k and stages must be >= 0, load_path in 0..2, waves 0, 4 or 8, mfma 0, 16 or 32");
     for (const KernelEntry &e : kernel_table())
         if (e.bm == tm && e.bn == tn && e.out_bf16 == out_bf16 && (desc->tile_k == 0 || e.bk == desc->tile_k) &&
             (desc->stages == 0 || e.stages == desc->stages) &&
             (desc->load_path == 0 || e.load_path == desc->load_path - 1) &&
-            (desc->waves == 0 || e.waves == desc->waves)) {
+            (desc->waves == 0 || e.waves == desc->waves) && (desc->mfma == 0 || e.mfma == desc->mfma)) {
             entry = &e;
             break;
         }
     if (entry == nullptr)
-        return fail(GEMM_ERR_UNSUPPORTED, "tile %dx%d (k %d, %d stages, load path %d) is not built", tm, tn,
-                    desc->tile_k, desc->stages, desc->load_path);
+        return fail(GEMM_ERR_UNSUPPORTED, "tile %dx%d (k %d, %d stages, load path %d, %d waves, mfma %d) is not built",
+                    tm, tn, desc->tile_k, desc->stages, desc->load_path, desc->waves, desc->mfma);
 
     auto plan = new (std::nothrow) gemm_plan();
     if (plan == nullptr)
