@@ -281,12 +281,25 @@ struct Mainloop {
         return (lane % C::CHUNKS) ^ lds_swizzle<C::BK>(r);
     }
 
+    // Paired loads (two waves per SIMD, two ring stages): on a full tile the
+    // first wave of each SIMD issues its own loads and those of its partner
+    // (wave + 4), whose rows are the same plus a fixed row shift, while the
+    // partner only computes. A wave stalled on issuing loads then always has
+    // a partner on its SIMD that keeps the matrix unit busy. Edge tiles, whose
+    // rows are clamped per lane, load as usual.
+    static constexpr bool PAIRED = C::WAVES == 8 && C::STAGES == 2 && C::LOAD_PATH == LOAD_DMA;
+    bool full_tile;
+    uint32_t a_shift, b_shift; // byte shift from a wave's rows to its partner's
+
     __device__ __forceinline__ void setup(const TileCtx<C> &t)
     {
         a_tile = t.a + (int64_t)t.row0 * t.lda;
         b_tile = t.b + (int64_t)t.col0 * t.ldb;
         a_rsrc = buffer_rsrc(a_tile);
         b_rsrc = buffer_rsrc(b_tile);
+        full_tile = t.vm == C::BM && t.vn == C::BN;
+        a_shift = (uint32_t)(4 * C::A_LOADS * C::ROWS_PER_LOAD * t.lda * 2);
+        b_shift = (uint32_t)(4 * C::B_LOADS * C::ROWS_PER_LOAD * t.ldb * 2);
         const int rl = lane / C::CHUNKS;
 #pragma unroll
         for (int i = 0; i < C::A_LOADS; ++i) {
@@ -303,14 +316,19 @@ struct Mainloop {
     // Issue load number `i` (0 .. LOADS-1; A loads first) of this wave's share
     // of k-tile kt into ring stage `stage`: one wave-wide 16-byte-per-lane
     // global->LDS load fills 1 KiB of the stage.
-    template <bool TAIL>
+    // Load number i of this wave's share, into the LDS slot of wave `lds_wave`
+    // (this wave, or its partner with PARTNER), rows shifted by the partner
+    // shift in the latter case.
+    template <bool TAIL, bool PARTNER = false>
     __device__ __forceinline__ void issue_one(int i, int kt, int stage, int k)
     {
         const bool is_a = i < C::A_LOADS;
         const int j = is_a ? i : i - C::A_LOADS;
         const int nl = is_a ? C::A_LOADS : C::B_LOADS;
+        const int lds_wave = PARTNER ? wave + 4 : wave;
         const uint32_t region = is_a ? 0u : (uint32_t)C::A_BYTES;
-        const uint32_t wbase = opaque_s((uint32_t)(stage * C::STAGE_BYTES) + region + (uint32_t)(wave * nl * 1024));
+        const uint32_t wbase =
+            opaque_s((uint32_t)(stage * C::STAGE_BYTES) + region + (uint32_t)(lds_wave * nl * 1024));
         uint32_t off = is_a ? a_off[j] : b_off[j];
         uint32_t soff = (uint32_t)kt * C::BK * 2;
         if constexpr (TAIL) {
@@ -320,12 +338,27 @@ struct Mainloop {
             off = off - c * 16 + min(kt * C::BK + c * 8, klast) * 2;
             soff = 0;
         }
+        if constexpr (PARTNER)
+            soff = uniform(soff + (is_a ? a_shift : b_shift));
         dma_load16(lds_address(smem + wbase + j * 1024), off, is_a ? a_rsrc : b_rsrc, soff);
     }
 
     template <bool TAIL>
     __device__ __forceinline__ void issue(int kt, int stage, int k)
     {
+        if constexpr (PAIRED) {
+            if (full_tile) {
+                if (wave < 4) {
+#pragma unroll
+                    for (int i = 0; i < C::LOADS; ++i)
+                        issue_one<TAIL>(i, kt, stage, k);
+#pragma unroll
+                    for (int i = 0; i < C::LOADS; ++i)
+                        issue_one<TAIL, true>(i, kt, stage, k);
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
             issue_one<TAIL>(i, kt, stage, k);
@@ -353,17 +386,35 @@ struct Mainloop {
 
     // Zero the k >= K part of the chunks this thread loaded into `stage`
     // (last k-tile only; this thread's loads of the stage have landed).
+    // The chunks a wave zeroes are the ones it loaded: with paired loads on a
+    // full tile, the first wave of each SIMD zeroes its own and its partner's
+    // (after its own load wait covered both) and the partner zeroes none.
     __device__ __forceinline__ void zero_k_tail(int kt, int stage, int k)
+    {
+        if constexpr (PAIRED) {
+            if (full_tile) {
+                if (wave < 4) {
+                    zero_k_tail_of(wave, kt, stage, k);
+                    zero_k_tail_of(wave + 4, kt, stage, k);
+                }
+                return;
+            }
+        }
+        zero_k_tail_of(wave, kt, stage, k);
+    }
+    __device__ __forceinline__ void zero_k_tail_of(int w, int kt, int stage, int k)
     {
         uint8_t *sa = smem + stage * C::STAGE_BYTES;
         uint8_t *sb = sa + C::A_BYTES;
         const int koff = kt * C::BK;
+        // the logical chunks of wave w's slots equal this wave's (the swizzle
+        // depends on the row modulo 16 and the partner shift is a multiple of 16)
 #pragma unroll
         for (int i = 0; i < C::A_LOADS; ++i)
-            zero_chunk_tail(sa + (wave * C::A_LOADS + i) * 1024 + lane * 16, koff + load_chunk(i, C::A_LOADS) * 8, k);
+            zero_chunk_tail(sa + (w * C::A_LOADS + i) * 1024 + lane * 16, koff + load_chunk(i, C::A_LOADS) * 8, k);
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i)
-            zero_chunk_tail(sb + (wave * C::B_LOADS + i) * 1024 + lane * 16, koff + load_chunk(i, C::B_LOADS) * 8, k);
+            zero_chunk_tail(sb + (w * C::B_LOADS + i) * 1024 + lane * 16, koff + load_chunk(i, C::B_LOADS) * 8, k);
     }
 
     // Byte offset, inside an MB-row block, of this lane's fragment for k-step
