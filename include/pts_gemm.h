@@ -68,9 +68,10 @@ typedef enum {
 typedef enum { GEMM_DTYPE_BF16 = 0, GEMM_DTYPE_F32 = 1 } gemm_dtype;
 typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout;
 /* STATIC: grid-stride. DYNAMIC: every tile claimed from one device-wide
- * counter. DYNAMIC_XCD: one counter per XCD (chiplet) over a contiguous range
- * of tiles, so the tiles in flight on an XCD share its L2; a worker whose
- * XCD's range is used up claims from the other ranges in turn.
+ * counter. DYNAMIC_XCD: one counter per XCD (chiplet) over the tiles the
+ * static schedule deals to that XCD (logical indices x, x+8, x+16, ...), so
+ * the tiles in flight on an XCD share its L2; a worker whose XCD's sequence is
+ * used up claims from the other XCDs' sequences in turn.
  * NONPERSISTENT: not a persistent kernel -- one workgroup per tile (grid =
  * tile count), dispatched by the hardware as compute units free up; the
  * comparison point the persistent schedules replace ("Schedules", section
@@ -183,7 +184,8 @@ gemm_status gemm_plan_query(const gemm_plan *plan, int64_t *num_tiles, int32_t *
  * `tile` is the tile's position in the plan's tile order (problems in turn;
  * inside a problem, groups of 8 tile rows walked column by column), `claim`
  * the scheduler's value that selected it (static: the logical grid-stride
- * index; dynamic: the counter value; per-XCD: XCD * 2^24 + counter value).
+ * index; dynamic: the counter value; per-XCD: XCD * 2^24 + counter value v,
+ * i.e. logical index XCD + 8 v).
  * Times are the 100 MHz device real-time counter; seq is the tile's place in
  * its worker's sequence; hw_id is the wave's HW_ID register and xcc_id its
  * XCC (chiplet) id; `cycles` counts shader-clock cycles over the same span,

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64) void sched_probe_kernel(int32_t num_tiles, int3
 
     TileScheduler sched{counters, num_tiles, num_workers, num_workers, w, mode, slots,
                         (int)(xcc_id_reg() % NUM_XCD), 0u};
-    Claimed cur = sched.first(leader);
+    Claimed cur = sched.first((int)threadIdx.x);
     int seq = 0;
     while (cur.pos < num_tiles) {
         sched.claim_ahead(leader);
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64) void sched_probe_kernel(int32_t num_tiles, int3
         while ((int64_t)(realtime() - t0) < work_ticks)
             __builtin_amdgcn_s_sleep(1);
         barrier_lds();
-        cur = sched.next(cur, leader, seq);
+        cur = sched.next(cur, (int)threadIdx.x, seq);
         ++seq;
     }
     if (leader)

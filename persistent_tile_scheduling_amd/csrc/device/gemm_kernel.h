@@ -1027,7 +1027,7 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     const bool tracing = trace != nullptr;
     const uint64_t t_worker0 = tracing ? realtime() : 0;
 
-    Claimed cur = sched.first(leader);
+    Claimed cur = sched.first(tid);
     int seq = 0;
     while (cur.pos < total_tiles) {
         const uint64_t t_tile0 = tracing ? realtime() : 0;
@@ -1051,7 +1051,7 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
         // The next tile's claim is resolved while the accumulators are staged
         // (its request went out a k-tile ago) and published by the staging
         // barrier, so no wave waits on it after the stores.
-        store_epilogue<C>(tc, acc, ml.wm, ml.wn, lane, tid, smem, [&] { sched.stage_next(leader, seq); });
+        store_epilogue<C>(tc, acc, ml.wm, ml.wn, lane, tid, smem, [&] { sched.stage_next(tid, seq); });
 
         if (tracing && leader) {
             TileTrace r;

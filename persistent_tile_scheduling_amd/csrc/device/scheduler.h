@@ -41,10 +41,12 @@
 // MI355X-specific variant (per-XCD claiming): the eight XCDs have separate
 // L2 caches, and one shared counter hands consecutive tiles to workers on
 // different XCDs, so no L2 sees its neighbours' A and B panels. Instead each
-// XCD owns a counter over a contiguous range of tile positions; a worker
-// claims from its own XCD's range and, once that is used up, from the other
-// ranges in turn (work stealing across XCDs); its loop ends only when every
-// range is used up. Every position is still handed out exactly once.
+// XCD owns a counter over the logical indices x, x+8, x+16, ... -- the tiles
+// the static schedule deals to that XCD's workers, round by round, in compact
+// blocks -- and its workers claim them in that order; once they are used up a
+// worker claims from the other XCDs' sequences in turn (work stealing across
+// XCDs); its loop ends only when every sequence is used up. Every position is
+// still handed out exactly once.
 //
 // Non-persistent comparison point: one workgroup per tile (grid = T), which
 // the hardware dispatches as compute units free up; each workgroup runs one
@@ -132,50 +134,82 @@ struct TileScheduler {
         pending = atomic_take(mode == SCHED_DYNAMIC ? CTR_CLAIM : ctr_xcd(xcd));
     }
 
-    // Turn the request into a tile (leader lane only). Single counter: the
-    // counter value is the position. Per-XCD counters: this XCD's range
-    // first; once it is used up, take from the other XCDs' ranges in turn;
-    // only when every range is used up has the request failed.
-    __device__ __forceinline__ Claimed resolve()
+    // XCD x's v-th claim is the logical index x + 8v: the same tiles, in the
+    // same rounds, that the static schedule deals to XCD x's workers.
+    __device__ __forceinline__ bool xcd_take(int x, uint32_t v, Claimed &out) const
     {
+        const uint32_t t = (uint32_t)x + (uint32_t)NUM_XCD * v;
+        if (v >= 0x1000000u || t >= (uint32_t)num_tiles)
+            return false;
+        out = Claimed{(int32_t)(x * 0x1000000 + v), static_position((int)t, num_tiles, round)};
+        return true;
+    }
+
+    // Turn the request into a tile. Called by every lane of the leader's
+    // wave (lane 0 holds `pending`); every lane returns the same result.
+    // Single counter: the counter value is the position. Per-XCD counters:
+    // this XCD's sequence first; once it is used up, lanes 1..7 look at the
+    // other seven counters at once (a counter that shows its sequence used up
+    // stays so) and the leader claims from the first, in turn from this XCD,
+    // that may still have work; only when none has is the request failed.
+    __device__ __forceinline__ Claimed resolve(int lane)
+    {
+        const uint32_t own = __builtin_amdgcn_readfirstlane(pending);
         if (mode == SCHED_DYNAMIC) {
-            const int32_t c = pending > 0x7FFFFFFFu ? 0x7FFFFFFF : (int32_t)pending;
+            const int32_t c = own > 0x7FFFFFFFu ? 0x7FFFFFFF : (int32_t)own;
             return Claimed{c, c};
         }
-        uint32_t v = pending;
+        Claimed c{0x7FFFFFFF, num_tiles};
+        if (xcd_take(xcd, own, c))
+            return c;
+        const int peek_x = (xcd + lane) % NUM_XCD;
+        bool avail = false;
+        if (lane >= 1 && lane < NUM_XCD) {
+            const uint32_t seen =
+                __hip_atomic_load(counters + ctr_xcd(peek_x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            avail = (uint64_t)peek_x + (uint64_t)NUM_XCD * seen < (uint64_t)num_tiles;
+        }
+        uint64_t mask = __ballot(avail);
 #pragma unroll 1
-        for (int d = 0; d < NUM_XCD; ++d) {
+        while (mask != 0) {
+            const int d = __builtin_ctzll(mask);
+            mask &= mask - 1;
             const int x = (xcd + d) % NUM_XCD;
-            const int lo = part_begin(num_tiles, NUM_XCD, x), hi = part_begin(num_tiles, NUM_XCD, x + 1);
-            if (d > 0)
+            uint32_t v = 0;
+            if (lane == 0)
                 v = atomic_take(ctr_xcd(x));
-            if (v < (uint32_t)(hi - lo))
-                return Claimed{(int32_t)(x * 0x1000000 + v), lo + (int32_t)v};
+            if (xcd_take(x, __builtin_amdgcn_readfirstlane(v), c))
+                return c;
         }
         return Claimed{0x7FFFFFFF, num_tiles};
     }
 
-    __device__ __forceinline__ Claimed publish_and_read(bool leader, int slot)
+    // Resolve in the leader's wave, write the result to LDS slot `slot`
+    // (lane 0), barrier, read it in every thread.
+    __device__ __forceinline__ Claimed publish_and_read(int tid, int slot)
     {
-        if (leader) {
-            const Claimed c = resolve();
-            slots[2 * slot] = c.claim;
-            slots[2 * slot + 1] = c.pos;
+        if (tid < 64) {
+            const Claimed c = resolve(tid);
+            if (tid == 0) {
+                slots[2 * slot] = c.claim;
+                slots[2 * slot + 1] = c.pos;
+            }
         }
         barrier_lds();
         return Claimed{uniform(slots[2 * slot]), uniform(slots[2 * slot + 1])};
     }
 
-    // First tile of this worker; all threads of the workgroup call it.
-    __device__ __forceinline__ Claimed first(bool leader)
+    // First tile of this worker; all threads of the workgroup call it (thread
+    // 0 is the leader).
+    __device__ __forceinline__ Claimed first(int tid)
     {
         if (mode == SCHED_STATIC || mode == SCHED_NONPERSISTENT) {
             const int32_t t = worker;
             return Claimed{t, t < num_tiles ? static_position(t, num_tiles, round) : num_tiles};
         }
-        if (leader)
+        if (tid == 0)
             issue();
-        return publish_and_read(leader, 0);
+        return publish_and_read(tid, 0);
     }
 
     // Issue the request for the tile after the current one (leader only).
@@ -190,23 +224,26 @@ struct TileScheduler {
     // The tile after `current` (all threads). For dynamic modes the pending
     // claim is resolved and published through LDS, which includes a barrier.
     // `seq` is the current tile's position in this worker's sequence.
-    __device__ __forceinline__ Claimed next(Claimed current, bool leader, int seq)
+    __device__ __forceinline__ Claimed next(Claimed current, int tid, int seq)
     {
         if (!claims())
             return next_computed(current);
-        return publish_and_read(leader, (seq + 1) & 1);
+        return publish_and_read(tid, (seq + 1) & 1);
     }
 
     // The same in two halves, for a caller that already has barriers to use:
-    // stage_next (leader; dynamic modes resolve the pending claim and write
-    // it to LDS), then, after at least one LDS barrier, read_next (all).
-    __device__ __forceinline__ void stage_next(bool leader, int seq)
+    // stage_next (all threads; dynamic modes resolve the pending claim in the
+    // leader's wave and write it to LDS), then, after at least one LDS
+    // barrier, read_next (all).
+    __device__ __forceinline__ void stage_next(int tid, int seq)
     {
-        if (claims() && leader) {
-            const Claimed c = resolve();
-            const int slot = (seq + 1) & 1;
-            slots[2 * slot] = c.claim;
-            slots[2 * slot + 1] = c.pos;
+        if (claims() && tid < 64) {
+            const Claimed c = resolve(tid);
+            if (tid == 0) {
+                const int slot = (seq + 1) & 1;
+                slots[2 * slot] = c.claim;
+                slots[2 * slot + 1] = c.pos;
+            }
         }
     }
 

@@ -107,26 +107,36 @@ def test_probe_static_at_scale(pts):
     assert per_worker == oracle.static_assignment(1000, 256)
 
 
-def _xcd_range(num_tiles, x):
-    q, rem = divmod(num_tiles, 8)
-    lo = x * q + min(x, rem)
-    return lo, lo + q + (1 if x < rem else 0)
+def _part_begin(n, parts, p):
+    q, rem = divmod(n, parts)
+    return p * q + min(p, rem)
 
 
-def check_xcd_claims(claims, worker_xcd, num_tiles):
-    """Per-XCD claiming: `claims` per worker are XCD * 2^24 + counter value."""
+def static_position(t, num_tiles, round_size):
+    """Position of logical index t: each round of round_size logical indices is
+    dealt so that the indices = x (mod 8) -- one XCD's workers -- get one
+    contiguous run of positions."""
+    base = (t // round_size) * round_size
+    r = min(round_size, num_tiles - base)
+    u = t - base
+    return base + _part_begin(r, 8, u % 8) + u // 8
+
+
+def check_xcd_claims(claims, worker_xcd, num_tiles, num_workers):
+    """Per-XCD claiming: `claims` per worker are XCD * 2^24 + counter value v,
+    meaning logical index XCD + 8 v at its static position."""
     positions = []
     for w, seq in enumerate(claims):
         dists, last = [], {}
         for c in seq:
             x, v = c >> 24, c & 0xFFFFFF
-            lo, hi = _xcd_range(num_tiles, x)
-            assert 0 <= x < 8 and lo + v < hi, f"worker {w}: claim {c} outside XCD {x}'s range"
-            positions.append(lo + v)
-            assert v > last.get(x, -1), f"worker {w}: claims in XCD {x}'s range not increasing"
+            t = x + 8 * v
+            assert 0 <= x < 8 and t < num_tiles, f"worker {w}: claim {c} outside XCD {x}'s sequence"
+            positions.append(static_position(t, num_tiles, num_workers))
+            assert v > last.get(x, -1), f"worker {w}: claims in XCD {x}'s sequence not increasing"
             last[x] = v
             dists.append((x - worker_xcd[w]) % 8)
-        assert dists == sorted(dists), f"worker {w} went back to a nearer XCD range: {dists}"
+        assert dists == sorted(dists), f"worker {w} went back to a nearer XCD: {dists}"
     assert sorted(positions) == list(range(num_tiles)), "positions not covered exactly once"
     return positions
 
@@ -189,13 +199,14 @@ def test_gemm_trace_covers_every_tile_once(pts, schedule, shapes, tile):
     assert np.all(tiles["xcc_id"] == workers["xcc_id"][tiles["worker"]])
     if schedule == "static":
         assert per_worker == oracle.static_assignment(nt, nw)
+        assert all(int(p) == static_position(int(c), nt, nw) for p, c in zip(tiles["tile"], tiles["claim"]))
     elif schedule == "nonpersistent":
         assert nw == nt and per_worker == [[w] for w in range(nw)]
     elif schedule == "dynamic":
         assert np.array_equal(tiles["claim"], tiles["tile"])
         oracle.check_dynamic_claims(per_worker, nt)
     else:
-        positions = check_xcd_claims(per_worker, (workers["xcc_id"] % 8).tolist(), nt)
+        positions = check_xcd_claims(per_worker, (workers["xcc_id"] % 8).tolist(), nt, nw)
         flat = [tiles["tile"][i] for i in order]
         assert positions == [int(t) for t in flat]
     U.check_counters(schedule, counters, nt, nw)
