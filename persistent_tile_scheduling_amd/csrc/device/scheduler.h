@@ -265,18 +265,24 @@ struct TileScheduler {
     }
 
     // End-of-kernel bookkeeping (leader only; after the worker's failed claim).
+    // Relaxed ordering suffices: every claim of this worker has returned (its
+    // value was read) before the exit increment is issued, so all claims of
+    // all workers are performed before the last exit increment, and the
+    // reset after it; device-scope atomics are performed at one coherent
+    // point. The next launch on the stream sees the reset at the kernel
+    // boundary. (Acquire/release here would add cache write-backs at exit.)
     __device__ __forceinline__ void finish(bool leader)
     {
         if (!claims() || !leader)
             return;
-        uint32_t old = __hip_atomic_fetch_add(counters + CTR_EXIT, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t old = __hip_atomic_fetch_add(counters + CTR_EXIT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (old == (uint32_t)num_workers - 1u) {
-            uint32_t total = __hip_atomic_exchange(counters + CTR_CLAIM, 0u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t total = __hip_atomic_exchange(counters + CTR_CLAIM, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             for (int x = 0; x < NUM_XCD; ++x)
-                total += __hip_atomic_exchange(counters + ctr_xcd(x), 0u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                total += __hip_atomic_exchange(counters + ctr_xcd(x), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(counters + CTR_FINAL, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_fetch_add(counters + CTR_RUNS, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(counters + CTR_EXIT, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(counters + CTR_EXIT, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 };
