@@ -227,21 +227,35 @@ __device__ __forceinline__ void raster_tile(int local, int tiles_m, int tiles_n,
     tn = within / rows;
 }
 
+// The plan's problem table is never written while a kernel runs: read it
+// through the constant address space, so a uniform index becomes scalar loads.
+typedef const __attribute__((address_space(4))) GroupDesc *ConstGroups;
+
+// Lane l of every wave holds problem l's first tile (or INT32_MAX past the
+// last problem): read once per worker, it turns the tile -> problem search
+// into one ballot (at most 64 problems, one per lane).
+__device__ __forceinline__ int load_group_begin(KernArgs args, int lane)
+{
+    const ConstGroups groups = (ConstGroups)args->groups;
+    return lane < args->group_count ? groups[lane].tile_begin : 0x7FFFFFFF;
+}
+
 template <class C>
-__device__ __forceinline__ TileCtx<C> decode_tile(KernArgs args, int t)
+__device__ __forceinline__ TileCtx<C> decode_tile(KernArgs args, int t, int group_begin)
 {
     // problem: the last g with tile_begin <= t (offsets are non-decreasing)
-    const GroupDesc *groups = args->groups;
-    int lo = 0, hi = args->group_count - 1;
-    while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (groups[mid].tile_begin <= t)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    const int g = uniform(lo);
-    const GroupDesc gd = groups[g];
+    const int g = __builtin_popcountll(__ballot(group_begin <= t)) - 1;
+    const ConstGroups gp = (ConstGroups)args->groups + g;
+    GroupDesc gd;
+    gd.m = gp->m;
+    gd.n = gp->n;
+    gd.k = gp->k;
+    gd.tiles_n = gp->tiles_n;
+    gd.tile_begin = gp->tile_begin;
+    gd.num_k_tiles = gp->num_k_tiles;
+    gd.lda = gp->lda;
+    gd.ldb = gp->ldb;
+    gd.ldd = gp->ldd;
     const int local = t - gd.tile_begin;
     int tm, tn;
     raster_tile(local, (gd.m + C::BM - 1) / C::BM, gd.tiles_n, tm, tn);
@@ -1003,6 +1017,10 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
 {
     (void)args_by_value;
     const KernArgs args = kernel_args();
+    const int group_begin = load_group_begin(args, (int)(threadIdx.x & 63));
+    // settle the load here, so no wait for it lands inside the tile loop
+    // (where it would also wait for the previous tile's stores)
+    wait_vmcnt<0>();
     constexpr int SMEM_BYTES = C::LDS_BYTES > Epilogue<C>::LDS_BYTES ? C::LDS_BYTES : Epilogue<C>::LDS_BYTES;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
     __shared__ int32_t sched_slots[4];
@@ -1032,7 +1050,7 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     while (cur.pos < total_tiles) {
         const uint64_t t_tile0 = tracing ? realtime() : 0;
         const uint64_t c_tile0 = tracing ? shader_cycles() : 0;
-        const TileCtx<C> tc = decode_tile<C>(args, cur.pos);
+        const TileCtx<C> tc = decode_tile<C>(args, cur.pos, group_begin);
 
         typename C::Acc acc[C::MI][C::NI];
 #pragma unroll
