@@ -128,3 +128,16 @@ def test_header_constants_match_the_binding(binding):
     enums = dict(re.findall(r"(GEMM_SCHEDULE_[A-Z_]+) = (\d+)", text))
     for name, value in enums.items():
         assert getattr(binding, name) == int(value), name
+
+
+@pytest.mark.parametrize("shape,fragment", [
+    ((256, 8, 8, 1 << 23, 8, 8), "32-bit"),              # a tile's rows of A span more than 2^31 bytes
+    ((8, 256, 8, 8, 1 << 23, 256), "32-bit"),            # same for the columns of B
+    ((1 << 30, 1 << 30, 8), "output tiles"),             # tile count beyond the claim encoding
+    ((1 << 31, 8, 8), "m, n, k"),
+])
+def test_plan_create_rejects_sizes_beyond_the_limits(binding, shape, fragment):
+    with pytest.raises(binding.GemmError) as ei:
+        binding.gemm_plan_create(binding.make_desc([shape]))
+    assert ei.value.status in (binding.GEMM_ERR_INVALID_VALUE, binding.GEMM_ERR_UNSUPPORTED)
+    assert fragment in str(ei.value)
