@@ -169,6 +169,35 @@ def test_m_or_n_zero_is_a_noop(pts):
         assert torch.all(d == 5.0)
 
 
+def test_leading_dimensions_at_the_32_bit_offset_limit(pts):
+    # A tile's load offsets are 32-bit byte offsets from its origin; the plan
+    # accepts leading dimensions up to 255 * ld * 2 + (k + 8) * 2 < 2^31. Use the
+    # largest such ld (about 2.5 GB per operand) with two tile rows / columns,
+    # so the second tile's rows sit just under the limit.
+    k = 64
+    ld = ((2**31 - 1 - (k + 8) * 2) // (255 * 2)) // 8 * 8
+    m = n = 300
+    a_bits, b_bits = _operands(m, n, k, 9, kind="integer")
+    ref = oracle.gemm(a_bits, b_bits, m, n, k)
+    for which in ("a", "b"):
+        U.log(f"leading dimension {ld} on {which}")
+        big = torch.zeros((m, ld), dtype=torch.bfloat16, device=U.DEV)
+        if which == "a":
+            big[:, :k] = U.bits_to_device(a_bits)
+            a, b, lda, ldb = big, U.bits_to_device(b_bits), ld, 0
+        else:
+            big[:, :k] = U.bits_to_device(b_bits)
+            a, b, lda, ldb = U.bits_to_device(a_bits), big, 0, ld
+        for sched in ("static", "dynamic_xcd"):
+            d, _, (tiles, _) = U.run_single(m, n, k, a, b, torch.float32, sched, lda=lda, ldb=ldb)
+            assert tiles == 4
+            U.check_exact(d, ref, f"ld {ld} on {which} {sched}")
+        del big
+        torch.cuda.empty_cache()
+    with pytest.raises(pts.GemmError):
+        pts.gemm_plan_create(pts.make_desc([(m, n, k, ld + 8, 0, 0)]))
+
+
 def test_tile_reuse_does_not_accumulate_across_tiles(pts):
     # one worker runs every tile: each tile's accumulators must restart at zero
     m, n, k = 512, 512, 128
