@@ -300,6 +300,7 @@ def main():
     ap.add_argument("--stages", type=int, default=0, help="LDS ring stages (0 = library default)")
     ap.add_argument("--load-path", type=int, default=0, help="1 = global->LDS, 2 = via registers (0 = default)")
     ap.add_argument("--waves", type=int, default=0, help="waves per workgroup, 4 or 8 (0 = default)")
+    ap.add_argument("--mfma", type=int, default=0, help="MFMA block edge, 16 or 32 (0 = default)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
@@ -325,7 +326,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     wl = workload(args.workload)
-    wl["tile"] = tuple(wl["tile"][:2]) + (args.tile_k, args.stages, args.load_path, args.waves)
+    wl["tile"] = tuple(wl["tile"][:2]) + (args.tile_k, args.stages, args.load_path, args.waves, args.mfma)
     print(f"# workload {args.workload}: {wl['desc']}", file=sys.stderr, flush=True)
     ops = make_operands(wl)
     conc = Concurrent(pts, wl["copy"], args.copy_cus) if wl["copy"] else None

@@ -92,6 +92,23 @@ __device__ __forceinline__ void dma_load16(uint32_t lds_addr, uint32_t voff, u32
                  : "memory");
 }
 
+// The same load, performed only when `on` (a wave-uniform flag): with `on`
+// false the load runs with no lanes enabled, so it neither reads memory nor
+// writes LDS. Used where a branch around the load would cost more than the
+// load itself. EXEC is restored before the statement ends; the wave's EXEC
+// must be all ones here (the callers run uniformly).
+__device__ __forceinline__ void dma_load16_if(uint32_t lds_addr, uint32_t voff, u32x4 rsrc, bool on)
+{
+    const uint32_t m = __builtin_amdgcn_readfirstlane(on ? 0xFFFFFFFFu : 0u);
+    const uint64_t mask = ((uint64_t)m << 32) | m;
+    uint64_t saved;
+    asm volatile("s_mov_b64 %0, exec\n\ts_mov_b64 exec, %5\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b64 exec, %0"
+                 : "=&s"(saved)
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(0u), "s"(mask)
+                 : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_address(const void *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;

@@ -112,6 +112,15 @@ template <> struct Mfma<16> {
     {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
     }
+    // The same instruction at a fixed place in the stream: these statements
+    // keep their program order with each other and with every memory access
+    // (the "memory" clobber), so a hand-placed interleaving of MFMAs, fragment
+    // reads and loads is issued as written. The accumulator stays in AGPRs
+    // with srcC tied to the destination.
+    static __device__ __forceinline__ void run_fixed(bf16x8 x, bf16x8 y, Acc &c)
+    {
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(x), "v"(y) : "memory");
+    }
 };
 
 // WAVES_M x WAVES_N waves per workgroup, one wave tile each. 2 x 2 gives one
@@ -302,6 +311,8 @@ struct Mainloop {
     // a partner on its SIMD that keeps the matrix unit busy. Edge tiles, whose
     // rows are clamped per lane, load as usual.
     static constexpr bool PAIRED = C::WAVES == 8 && C::STAGES == 2 && C::LOAD_PATH == LOAD_DMA;
+    // One wave per SIMD with 16x16 blocks: the hand-laid k loop below.
+    static constexpr bool SINGLE = C::WAVES == 4 && C::MB == 16;
     bool full_tile;
     uint32_t a_shift, b_shift; // byte shift from a wave's rows to its partner's
 
@@ -325,6 +336,34 @@ struct Mainloop {
             const int r = (wave * C::B_LOADS + i) * C::ROWS_PER_LOAD + rl;
             b_off[i] = (uint32_t)((int64_t)min(r, t.vn - 1) * t.ldb * 2) + load_chunk(i, C::B_LOADS) * 16;
         }
+        if constexpr (SINGLE) {
+            // last 16-byte chunk start inside the rows' readable extent, as a
+            // byte limit on the k-tile offset of each load's chunk
+            const int klast = ((t.k + 7) & ~7) - 8;
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+                k_lim[p] = (klast - load_chunk(p, C::A_LOADS) * 8) * 2;
+        }
+    }
+
+    // The one-wave layout's loads. A load's chunk offset is clamped to the
+    // last chunk start inside the rows: for every k-tile but a last one that
+    // ends inside a k-tile this is the chunk itself, for that one it is what
+    // the tail form computes. So one branch-free form serves every k-tile,
+    // and a load past the last k-tile is masked off instead of branched over.
+    // The logical chunk of load i depends on i only through its parity (the
+    // swizzle repeats every 16 rows and a load covers 8), for A and B alike.
+    int k_lim[2];
+    __device__ __forceinline__ void issue_masked(int i, int kt, int stage, bool on)
+    {
+        static_assert(C::A_LOADS == C::B_LOADS && C::A_LOADS % 2 == 0 && C::ROWS_PER_LOAD == 8, "chunk parity");
+        const bool is_a = i < C::A_LOADS;
+        const int j = is_a ? i : i - C::A_LOADS;
+        const uint32_t region = is_a ? 0u : (uint32_t)C::A_BYTES;
+        const uint32_t wbase =
+            opaque_s((uint32_t)(stage * C::STAGE_BYTES) + region + (uint32_t)(wave * C::A_LOADS * 1024));
+        const uint32_t off = (is_a ? a_off[j] : b_off[j]) + (uint32_t)min(kt * C::BK * 2, k_lim[j & 1]);
+        dma_load16_if(lds_address(smem + wbase + j * 1024), off, is_a ? a_rsrc : b_rsrc, on);
     }
 
     // Issue load number `i` (0 .. LOADS-1; A loads first) of this wave's share
@@ -540,6 +579,8 @@ struct Mainloop {
             run_regs(t, acc, on_last_stage);
         else if constexpr (C::STAGES >= 3)
             run_spread(t, acc, on_last_stage);
+        else if constexpr (C::MB == 16 && C::WAVES == 4)
+            run_single(t, acc, on_last_stage);
         else if constexpr (C::MB == 16)
             run_burst_rolling(t, acc, on_last_stage);
         else
@@ -644,6 +685,101 @@ struct Mainloop {
             // the last k-tile: a stage nobody writes any more; unused).
             rolling_step<(C::KSTEPS - 1) & 1>(f, acc, stage ^ 1, 0);
         }
+    }
+
+    // ---- one wave per SIMD (16x16 blocks) ------------------------------------
+    // A wave owns 128x128 of the tile: 64 MFMAs per k-step, 16 fragment reads,
+    // 256 accumulators (all AGPRs), and both fragment sets fit in registers.
+    // With no second wave on the SIMD to cover a stall, the k-step is laid out
+    // by hand: the next k-step's fragment reads and, in the second k-step of a
+    // k-tile, this wave's loads of k-tile kt + 2 are spread between the MFMAs,
+    // so neither LDS nor the load queue ever holds up the matrix unit in one
+    // burst. The reads end well before the k-step does, so the stage barrier
+    // finds them complete.
+    static constexpr int S_MFMAS = C::MI * C::NI;
+    static constexpr int S_READS = C::MI + C::NI;
+    static constexpr int READ_EVERY = 3; // one read after every third MFMA
+    static constexpr int LOAD_EVERY = 2; // one load after every second MFMA
+
+    // Fragment read r of a k-step, in the order the next k-step first needs
+    // them: A0, B0 .. B(NI-1), A1 .. A(MI-1).
+    __device__ __forceinline__ void read_frag(Frags &f, int r, const uint8_t *sa, const uint8_t *sb,
+                                              uint32_t foff) const
+    {
+        if (r == 0)
+            f.a[0] = *(const bf16x8 *)(sa + foff);
+        else if (r <= C::NI)
+            f.b[r - 1] = *(const bf16x8 *)(sb + foff + (r - 1) * C::MB * C::ROW_BYTES);
+        else
+            f.a[r - C::NI] = *(const bf16x8 *)(sa + foff + (r - C::NI) * C::MB * C::ROW_BYTES);
+    }
+
+    // One k-step from `cur`, reading k-step rks of stage rstage into `nxt`.
+    // With LOADS, this wave's loads of k-tile lkt go into stage lstage between
+    // the MFMAs, masked off unless `on`.
+    template <bool LOADS>
+    __device__ __forceinline__ void single_step(const Frags &cur, Frags &nxt, typename C::Acc (&acc)[C::MI][C::NI],
+                                                int rstage, int rks, int lkt, int lstage, bool on)
+    {
+        static_assert(S_READS * READ_EVERY <= S_MFMAS && C::LOADS * LOAD_EVERY <= S_MFMAS, "slots");
+        const uint8_t *sa = a_base(rstage), *sb = b_base(rstage);
+        const uint32_t foff = frag_off[rks];
+#pragma unroll
+        for (int x = 0; x < S_MFMAS; ++x) {
+            const int mi = x / C::NI, ni = x % C::NI;
+            C::Op::run_fixed(cur.b[ni], cur.a[mi], acc[mi][ni]);
+            if (x % READ_EVERY == 0 && x / READ_EVERY < S_READS)
+                read_frag(nxt, x / READ_EVERY, sa, sb, foff);
+            if (LOADS && x % LOAD_EVERY == LOAD_EVERY - 1 && x / LOAD_EVERY < C::LOADS)
+                issue_masked(x / LOAD_EVERY, lkt, lstage, on);
+        }
+    }
+
+    // Every k-tile has the same shape: k-step 0 (reading k-step 1), the
+    // barrier that readies k-tile kt + 1, k-step 1 (reading k-step 0 of kt + 1
+    // and loading kt + 2). Past the end the reads fetch a stage nobody uses
+    // and the loads are masked off. With no branch around the MFMAs the
+    // accumulators stay in AGPRs for the whole loop.
+    template <class Hook>
+    __device__ __forceinline__ void run_single(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI],
+                                               Hook &on_last_stage)
+    {
+        static_assert(C::STAGES == 2 && C::KSTEPS == 2 && C::LOAD_PATH == LOAD_DMA && !PAIRED, "one-wave layout");
+        const int nk = t.nk;
+        if (nk == 0) {
+            on_last_stage();
+            return; // the accumulators keep their zeros
+        }
+        issue_any(0, 0, t.k, nk);
+        stage_ready(0, t);
+        if (1 < nk)
+            issue_any(1, 1, t.k, nk);
+        if (nk == 1)
+            on_last_stage();
+        Frags f0, f1;
+        load_frags(0, 0, f0);
+        // The zeros must reach the accumulators before the first MFMA reads
+        // them, and the compiler does not see the MFMAs as such: pin the
+        // zeroing here and leave the write-to-read latency.
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < C::NI; ++ni)
+                asm volatile("" : "+a"(acc[mi][ni]));
+        asm volatile("s_nop 4" ::: "memory");
+        for (int kt = 0; kt < nk; ++kt) {
+            const int stage = kt & 1;
+            single_step<false>(f0, f1, acc, stage, 1, 0, 0, false);
+            if (kt + 1 < nk)
+                stage_ready(kt + 1, t);
+            if (kt + 2 == nk)
+                on_last_stage();
+            single_step<true>(f1, f0, acc, stage ^ 1, 0, kt + 2, stage, kt + 2 < nk);
+        }
+        // The accumulators were last written by MFMAs the compiler sees only
+        // as assembly: leave the matrix unit's result latency before anything
+        // reads them.
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     }
 
     // ---- register path ----------------------------------------------------

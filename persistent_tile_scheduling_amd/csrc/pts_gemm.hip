@@ -72,6 +72,8 @@ const std::vector<KernelEntry> &kernel_table()
         make_entry<256, 256, 32, 4, true, pts::LOAD_DMA, 2, 4>(),
         make_entry<256, 256, 32, 4, false, pts::LOAD_DMA, 2, 4>(),
         make_entry<256, 256, 64, 2, true>(),  make_entry<256, 256, 64, 2, false>(),
+        make_entry<256, 256, 64, 2, true, pts::LOAD_DMA, 2, 2, 16>(),
+        make_entry<256, 256, 64, 2, false, pts::LOAD_DMA, 2, 2, 16>(),
         make_entry<256, 256, 32, 4, true>(),  make_entry<256, 256, 32, 4, false>(),
         make_entry<256, 256, 64, 2, true, pts::LOAD_REG>(), make_entry<256, 256, 64, 2, false, pts::LOAD_REG>(),
         make_entry<128, 128, 64, 2, true>(),  make_entry<128, 128, 64, 2, false>(),
