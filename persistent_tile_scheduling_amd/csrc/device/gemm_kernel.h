@@ -202,6 +202,7 @@ struct TileCtx {
     int group;
     int row0, col0, vm, vn; // tile origin and valid extent
     int k, nk;
+    int kt0; // first k-tile of the tile's k order (see k_phase)
     int64_t lda, ldb, ldd;
     const uint16_t *a;
     const uint16_t *b;
@@ -234,6 +235,23 @@ __device__ __forceinline__ void raster_tile(int local, int tiles_m, int tiles_n,
     const int within = local - first_row * tiles_n;
     tm = first_row + within % rows;
     tn = within / rows;
+}
+
+// Where a tile's k loop starts. Each compute die (XCD) works on a compact
+// block of tiles whose A and B panels its L2 shares, so within a block every
+// tile walks k in the same order. Across blocks the start is rotated by
+// K_PHASE k-tiles per block, so the dies do not all request the same k-slice
+// of memory at once. Each tile still sums every k-tile exactly once, in an
+// order fixed by its position alone, so every schedule and worker count
+// computes the same bits. A block is K_PHASE_BLOCK consecutive positions:
+// what the static dealing gives one die per round with one workgroup on each
+// of the 256 compute units (32 per die).
+constexpr int K_PHASE = 8;
+constexpr int K_PHASE_BLOCK = 32;
+
+__device__ __forceinline__ int k_phase(int pos, int nk)
+{
+    return nk > 0 ? ((pos / K_PHASE_BLOCK) % NUM_XCD) * K_PHASE % nk : 0;
 }
 
 // The plan's problem table is never written while a kernel runs: read it
@@ -276,6 +294,7 @@ __device__ __forceinline__ TileCtx<C> decode_tile(KernArgs args, int t, int grou
     c.vn = min(C::BN, gd.n - c.col0);
     c.k = gd.k;
     c.nk = gd.num_k_tiles;
+    c.kt0 = k_phase(t, c.nk);
     c.lda = gd.lda;
     c.ldb = gd.ldb;
     c.ldd = gd.ldd;
@@ -316,8 +335,21 @@ struct Mainloop {
     bool full_tile;
     uint32_t a_shift, b_shift; // byte shift from a wave's rows to its partner's
 
+    // The k loop visits k-tiles in the tile's rotated order: iteration kt
+    // holds k-tile phys(kt). Every k offset and every "is this the partial
+    // last k-tile" test goes through it.
+    int kt0, nk_all;
+    __device__ __forceinline__ int phys(int kt) const
+    {
+        const int p = kt + kt0;
+        return p >= nk_all ? p - nk_all : p;
+    }
+    __device__ __forceinline__ bool is_tail(int kt, int k) const { return (k % C::BK) != 0 && phys(kt) == nk_all - 1; }
+
     __device__ __forceinline__ void setup(const TileCtx<C> &t)
     {
+        kt0 = t.kt0;
+        nk_all = t.nk;
         a_tile = t.a + (int64_t)t.row0 * t.lda;
         b_tile = t.b + (int64_t)t.col0 * t.ldb;
         a_rsrc = buffer_rsrc(a_tile);
@@ -362,7 +394,7 @@ struct Mainloop {
         const uint32_t region = is_a ? 0u : (uint32_t)C::A_BYTES;
         const uint32_t wbase =
             opaque_s((uint32_t)(stage * C::STAGE_BYTES) + region + (uint32_t)(wave * C::A_LOADS * 1024));
-        const uint32_t off = (is_a ? a_off[j] : b_off[j]) + (uint32_t)min(kt * C::BK * 2, k_lim[j & 1]);
+        const uint32_t off = (is_a ? a_off[j] : b_off[j]) + (uint32_t)min(phys(kt) * C::BK * 2, k_lim[j & 1]);
         dma_load16_if(lds_address(smem + wbase + j * 1024), off, is_a ? a_rsrc : b_rsrc, on);
     }
 
@@ -383,12 +415,12 @@ struct Mainloop {
         const uint32_t wbase =
             opaque_s((uint32_t)(stage * C::STAGE_BYTES) + region + (uint32_t)(lds_wave * nl * 1024));
         uint32_t off = is_a ? a_off[j] : b_off[j];
-        uint32_t soff = (uint32_t)kt * C::BK * 2;
+        uint32_t soff = (uint32_t)phys(kt) * C::BK * 2;
         if constexpr (TAIL) {
             // last 16-byte chunk start inside the rows' readable extent
             const int klast = ((k + 7) & ~7) - 8;
             const int c = load_chunk(j, nl);
-            off = off - c * 16 + min(kt * C::BK + c * 8, klast) * 2;
+            off = off - c * 16 + min(phys(kt) * C::BK + c * 8, klast) * 2;
             soff = 0;
         }
         if constexpr (PARTNER)
@@ -419,7 +451,8 @@ struct Mainloop {
 
     __device__ __forceinline__ void issue_any(int kt, int stage, int k, int nk)
     {
-        if ((k % C::BK) != 0 && kt == nk - 1)
+        (void)nk;
+        if (is_tail(kt, k))
             issue<true>(kt, stage, k);
         else
             issue<false>(kt, stage, k);
@@ -459,7 +492,7 @@ struct Mainloop {
     {
         uint8_t *sa = smem + stage * C::STAGE_BYTES;
         uint8_t *sb = sa + C::A_BYTES;
-        const int koff = kt * C::BK;
+        const int koff = phys(kt) * C::BK;
         // the logical chunks of wave w's slots equal this wave's (the swizzle
         // depends on the row modulo 16 and the partner shift is a multiple of 16)
 #pragma unroll
@@ -523,7 +556,7 @@ struct Mainloop {
     {
         constexpr int MFMAS = C::MI * C::NI;
         constexpr int EVERY = MFMAS / COUNT > 0 ? MFMAS / COUNT : 1;
-        const bool tail = (t.k % C::BK) != 0 && dma_kt == t.nk - 1;
+        const bool tail = is_tail(dma_kt, t.k);
 #pragma unroll
         for (int x = 0; x < MFMAS; ++x) {
             const int mi = x / C::NI, ni = x % C::NI;
@@ -563,7 +596,7 @@ struct Mainloop {
     __device__ __forceinline__ void stage_ready(int kt, const TileCtx<C> &t)
     {
         wait_stage_loads<C, C::STAGES - 2>(min(C::STAGES - 2, t.nk - 1 - kt));
-        if ((t.k % C::BK) != 0 && kt == t.nk - 1)
+        if (is_tail(kt, t.k))
             zero_k_tail(kt, kt % C::STAGES, t.k);
         barrier_lds();
     }
@@ -806,7 +839,7 @@ struct Mainloop {
         const int nl = is_a ? C::A_LOADS : C::B_LOADS;
         const int c = load_chunk(j, nl);
         const int klast = ((t.k + 7) & ~7) - 8;
-        const uint32_t off = (is_a ? a_off[j] : b_off[j]) - c * 16 + min(kt * C::BK + c * 8, klast) * 2;
+        const uint32_t off = (is_a ? a_off[j] : b_off[j]) - c * 16 + min(phys(kt) * C::BK + c * 8, klast) * 2;
         staged[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_of(is_a ? a_tile : b_tile), off, 0, 0);
     }
 
@@ -889,7 +922,6 @@ struct Mainloop {
             on_last_stage();
             return;
         }
-        const bool ktail = (t.k % C::BK) != 0;
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
             gload_one(i, 0, t);
@@ -899,7 +931,7 @@ struct Mainloop {
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
             gload_one(i, min(1, nk - 1), t);
-        if (ktail && nk == 1) {
+        if (is_tail(0, t.k) && nk == 1) {
             wait_lgkmcnt0();
             zero_k_tail(0, 0, t.k);
         }
@@ -911,7 +943,7 @@ struct Mainloop {
             const int kt_load = min(kt + 2, nk - 1);
             regs_steps<0>(f, acc, stage, kt_load, t);
             if (kt + 1 < nk) {
-                if (ktail && kt + 1 == nk - 1) {
+                if (is_tail(kt + 1, t.k)) {
                     wait_lgkmcnt0();
                     zero_k_tail(kt + 1, stage ^ 1, t.k);
                 }
@@ -989,7 +1021,7 @@ struct Mainloop {
             issue_any(s, s, t.k, nk);
         // k-tile 0: its loads were the oldest of the prologue
         wait_stage_loads<C, C::STAGES - 1>(min(C::STAGES - 1, nk - 1));
-        if ((t.k % C::BK) != 0 && nk == 1)
+        if (nk == 1 && is_tail(0, t.k))
             zero_k_tail(0, 0, t.k);
         barrier_lds();
         if (nk == 1)
@@ -1017,7 +1049,7 @@ struct Mainloop {
                         min(C::STAGES - 3, nk - 1 - (kt + 2)));
                 else
                     wait_stage_loads<C, C::STAGES - 2>(min(C::STAGES - 2, nk - 1 - (kt + 1)));
-                if ((t.k % C::BK) != 0 && kt + 1 == nk - 1)
+                if (is_tail(kt + 1, t.k))
                     zero_k_tail(kt + 1, (kt + 1) % C::STAGES, t.k);
                 barrier_lds();
                 if (kt + 2 == nk)

@@ -94,6 +94,35 @@ def test_integer_exact_sweep(pts, tile, out_dtype):
             U.check_exact(d[:m, :n], ref, f"{(m, n, k)} tile {tile} {sched}")
 
 
+_ROTATED_CASE = {}
+
+
+def _rotated_case():
+    # 2304 x 2304 x 1000: 81 tiles of 256 (1296 of 64), so tiles past the first
+    # 32 positions start their k loop part-way through K, and the partial last
+    # k-tile (K = 15 * 64 + 40) is visited in the middle of the loop
+    if not _ROTATED_CASE:
+        m = n = 2304
+        k = 1000
+        lda = ldb = _padded_ld(k)
+        a_bits, b_bits = _operands(m, n, k, 11, kind="integer", lda=lda, ldb=ldb)
+        _ROTATED_CASE.update(m=m, n=n, k=k, lda=lda, ldb=ldb, a_bits=a_bits, b_bits=b_bits,
+                             ref=oracle.gemm(a_bits, b_bits, m, n, k, lda=lda, ldb=ldb))
+    return _ROTATED_CASE
+
+
+@pytest.mark.parametrize("tile", KERNELS)
+def test_rotated_k_order_with_k_tail(pts, tile):
+    c = _rotated_case()
+    a, b = U.bits_to_device(c["a_bits"]), U.bits_to_device(c["b_bits"])
+    for out_dtype in (torch.float32, torch.bfloat16):
+        for sched in SCHEDULES:
+            U.log(f"rotated k order tile {tile} {out_dtype} {sched}")
+            d, _, _ = U.run_single(c["m"], c["n"], c["k"], a, b, out_dtype, sched, tile=tile, lda=c["lda"],
+                                   ldb=c["ldb"])
+            U.check_exact(d[:c["m"], :c["n"]], c["ref"], f"rotated tile {tile} {out_dtype} {sched}")
+
+
 # ---------------------------------------------------------------------------
 # Random inputs, ragged medium shapes, full oracle; D padding untouched
 # ---------------------------------------------------------------------------
