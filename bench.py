@@ -107,7 +107,7 @@ def time_headline(pts, wl, ops, schedule, steps, warmup, conc=None):
     import torch
     stream = torch.cuda.Stream()
     flops = sum(2.0 * m * n * k for (m, n, k) in wl["shapes"])
-    with pts.Plan(wl["shapes"], wl["out"], wl["tile"], schedule) as plan:
+    with pts.Plan(wl["shapes"], wl["out"], wl["tile"], schedule, 0, wl["flags"]) as plan:
         for _ in range(warmup):
             if conc is not None:
                 conc.launch()
@@ -146,7 +146,7 @@ def compare_schedules(pts, wl, ops, schedules, rounds, conc=None):
     import torch
     stream = torch.cuda.Stream()
     flops = sum(2.0 * m * n * k for (m, n, k) in wl["shapes"])
-    plans = {s: pts.Plan(wl["shapes"], wl["out"], wl["tile"], s) for s in schedules}
+    plans = {s: pts.Plan(wl["shapes"], wl["out"], wl["tile"], s, 0, wl["flags"]) for s in schedules}
     times = {s: [] for s in schedules}
     try:
         for s in schedules:
@@ -180,7 +180,7 @@ def tail_idle(pts, wl, ops, schedule, conc=None):
     """Fraction of worker-time idle after each worker's last tile, from the trace."""
     import torch
     stream = torch.cuda.Stream()
-    with pts.Plan(wl["shapes"], wl["out"], wl["tile"], schedule) as plan:
+    with pts.Plan(wl["shapes"], wl["out"], wl["tile"], schedule, 0, wl["flags"]) as plan:
         buf = torch.zeros(plan.trace_bytes() // 4 + 4, dtype=torch.int32, device="cuda")
         plan.set_trace(buf)
         for _ in range(2):
@@ -301,6 +301,8 @@ def main():
     ap.add_argument("--load-path", type=int, default=0, help="1 = global->LDS, 2 = via registers (0 = default)")
     ap.add_argument("--waves", type=int, default=0, help="waves per workgroup, 4 or 8 (0 = default)")
     ap.add_argument("--mfma", type=int, default=0, help="MFMA block edge, 16 or 32 (0 = default)")
+    ap.add_argument("--stage-sync", default="barrier", choices=["barrier", "fused", "merged"],
+                    help="stage hand-off: workgroup barrier, or LDS full/empty counters (2 or 3 words per stage)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true")
@@ -327,6 +329,8 @@ def main():
         sys.exit(1)
     wl = workload(args.workload)
     wl["tile"] = tuple(wl["tile"][:2]) + (args.tile_k, args.stages, args.load_path, args.waves, args.mfma)
+    wl["flags"] = {"barrier": 0, "fused": pts.GEMM_FLAG_STAGE_FLAGS_FUSED,
+                   "merged": pts.GEMM_FLAG_STAGE_FLAGS_MERGED}[args.stage_sync]
     print(f"# workload {args.workload}: {wl['desc']}", file=sys.stderr, flush=True)
     ops = make_operands(wl)
     conc = Concurrent(pts, wl["copy"], args.copy_cus) if wl["copy"] else None
@@ -380,11 +384,11 @@ def main():
         "config": {"workload": wl["desc"], "schedule": head_sched,
                    "shapes": wl["shapes"] if len(wl["shapes"]) <= 4 else f"{len(wl['shapes'])} problems",
                    "tile": list(wl["tile"]), "out_dtype": str(wl["out"]).replace("torch.", ""),
-                   "copy_cus": args.copy_cus if wl["copy"] else None},
+                   "copy_cus": args.copy_cus if wl["copy"] else None, "stage_sync": args.stage_sync},
         "roofline": {"bound": "mfma", "achieved": round(head["kernel_tflops"], 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(head["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(args.workload, head_sched, wl),
+                     "traffic": measured_traffic(args.workload, head_sched, wl) if args.stage_sync == "barrier" else None,
                      "kernel": "pts::gemm_persistent_kernel", "flop_per_launch": flops,
                      "kernel_ms_avg": round(head["kernel_ms_avg"], 5)},
         "schedules": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}

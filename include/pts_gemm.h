@@ -97,6 +97,24 @@ typedef struct {
 
 /* Plan flags. */
 #define GEMM_FLAG_NONE 0u
+/*
+ * Stage hand-off inside the k loop (persistent-kernel page, pipeline groups:
+ * "FusedMerge" and "Merge" barrier layouts). By default one workgroup barrier
+ * per ring stage serves as the stage's full and empty barrier at once. With
+ * one of these flags the stages instead carry arrive counters in LDS, and a
+ * wave waits only for the stage it needs next:
+ *   GEMM_FLAG_STAGE_FLAGS_FUSED:  one full and one empty counter per stage
+ *                                 (2 words per stage; all loads of a stage
+ *                                 arrive on the one full counter);
+ *   GEMM_FLAG_STAGE_FLAGS_MERGED: a full counter for A, a full counter for B,
+ *                                 one empty counter (3 words per stage).
+ * Results are bit-identical to the barrier form. Built for the 8-wave 16x16
+ * two-stage kernel (the 256x256 default); other kernels, or both flags at
+ * once, give GEMM_ERR_UNSUPPORTED. A device-side wait is bounded: one that runs
+ * out is counted in out[4] of gemm_plan_read_counters, and that run's D is void.
+ */
+#define GEMM_FLAG_STAGE_FLAGS_FUSED 1u
+#define GEMM_FLAG_STAGE_FLAGS_MERGED 2u
 
 typedef struct {
     int32_t group_count;       /* 1 = one GEMM; 2..GEMM_MAX_GROUPS = grouped, one launch */
@@ -204,9 +222,11 @@ gemm_status gemm_plan_set_trace(gemm_plan *plan, void *device_buf, size_t bytes)
  * live claim counters, summed (0 between dynamic runs), out[1] the live exit counter
  * (0 between runs), out[2] the total number of claims in the last dynamic run
  * (single counter: tiles + workers, since every worker's loop ends on exactly
- * one failed claim), out[3] the number of dynamic runs completed.
+ * one failed claim), out[3] the number of dynamic runs completed, out[4] the
+ * number of stage-flag waits that ran out since the plan was created (always 0
+ * unless the stage hand-off is broken; see GEMM_FLAG_STAGE_FLAGS_FUSED).
  */
-gemm_status gemm_plan_read_counters(const gemm_plan *plan, uint32_t out[4]);
+gemm_status gemm_plan_read_counters(const gemm_plan *plan, uint32_t out[5]);
 
 /*
  * Grid-stride int16 copy dst[i] = src[i] for 0 <= i < n, 16 bytes per lane per

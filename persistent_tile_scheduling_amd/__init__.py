@@ -36,6 +36,8 @@ GEMM_SCHEDULE_NONPERSISTENT = 3
 GEMM_SCHED_COUNTER_BYTES = 36864
 GEMM_MAX_GROUPS = 64
 GEMM_FLAG_NONE = 0
+GEMM_FLAG_STAGE_FLAGS_FUSED = 1
+GEMM_FLAG_STAGE_FLAGS_MERGED = 2
 
 TILE_TRACE_BYTES = 56
 WORKER_TRACE_BYTES = 32
@@ -178,7 +180,7 @@ def gemm_plan_set_trace(plan: int, device_buf, nbytes: int) -> None:
 
 
 def gemm_plan_read_counters(plan: int) -> list[int]:
-    out = (ctypes.c_uint32 * 4)()
+    out = (ctypes.c_uint32 * 5)()
     _check(_lib.gemm_plan_read_counters(ctypes.c_void_p(plan), out))
     return list(out)
 
@@ -217,7 +219,7 @@ class Plan:
     ``tile``: (tile_m, tile_n[, tile_k, stages, load_path, waves]), 0 = default."""
 
     def __init__(self, shapes, out_dtype=torch.float32, tile=(0, 0), schedule: str | int = "static",
-                 num_workers: int = 0):
+                 num_workers: int = 0, flags: int = GEMM_FLAG_NONE):
         if isinstance(schedule, str):
             schedule = {"static": GEMM_SCHEDULE_STATIC, "dynamic": GEMM_SCHEDULE_DYNAMIC,
                         "dynamic_xcd": GEMM_SCHEDULE_DYNAMIC_XCD,
@@ -226,7 +228,7 @@ class Plan:
         self.shapes = [tuple(s) for s in shapes]
         self.out_dtype = out_dtype
         self.schedule = schedule
-        self.desc = make_desc(self.shapes, dtype_d, tile, schedule, num_workers)
+        self.desc = make_desc(self.shapes, dtype_d, tile, schedule, num_workers, flags)
         self.handle = gemm_plan_create(self.desc)
         self.num_tiles, self.num_workers, self.lds_bytes = gemm_plan_query(self.handle)
 

@@ -78,11 +78,18 @@ struct GemmArgs {
     int32_t num_workers;
     int32_t schedule;
     int32_t round;     // static dealing width (see static_position)
-    int32_t pad;
+    int32_t sync;      // stage hand-off: SYNC_BARRIER, SYNC_FUSED or SYNC_MERGED
     uint64_t d_vec_ok; // bit g: problem g's D rows allow vector stores
     const uint16_t *a[PTS_MAX_GROUPS];
     const uint16_t *b[PTS_MAX_GROUPS];
     void *d[PTS_MAX_GROUPS];
+};
+
+// How a ring stage is handed from its loads to its readers and back.
+enum : int {
+    SYNC_BARRIER = 0, // one workgroup barrier per stage serves as full and empty
+    SYNC_FUSED = 1,   // per stage: one full and one empty arrive counter (2 words per stage)
+    SYNC_MERGED = 2   // per stage: full for A, full for B, one empty (3 words per stage)
 };
 
 // LOAD_PATH: how a ring stage is filled.
@@ -589,6 +596,104 @@ struct Mainloop {
             __builtin_amdgcn_sched_group_barrier(0x100, READS - PAIRS, 0);
     }
 
+    // ---- stage flags --------------------------------------------------------
+    // The pages' per-stage full and empty barriers, as arrive counters in LDS
+    // in place of the workgroup barrier (two-stage paired loop only). Every use
+    // of a stage adds exactly FLAG_UNIT to each of its words: the loading waves
+    // split it on full (all 8 waves load on an edge tile, the first 4 on a full
+    // tile), every wave adds 1 to empty once it has issued its last read of the
+    // stage. The counters only grow, so a wave waits for "at least the count of
+    // this use" and no reset is needed between tiles: `uses` counts this
+    // worker's earlier fills of each stage. LDS operations of one wave are
+    // performed in order, so an arrive issued after a wave's reads (or after its
+    // load wait) is seen only after them.
+    static constexpr uint32_t FLAG_UNIT = C::WAVES;
+    static constexpr uint32_t SPIN_LIMIT = 1u << 15; // ~2M cycles: far beyond any legitimate wait
+    static constexpr int W_FULL = 0, W_FULL_B = 2, W_EMPTY = 4; // word offsets (+ stage)
+    __attribute__((address_space(3))) uint32_t *sflags;
+    uint32_t *stall_ctr; // device counter of waits that ran out
+    int sync;
+    uint32_t uses0, uses1;
+    bool broken; // a wait ran out: stop waiting (the plan's stall counter says the result is void)
+
+    __device__ __forceinline__ uint32_t use_of(int kt) const { return ((kt & 1) ? uses1 : uses0) + (uint32_t)(kt >> 1); }
+    __device__ __forceinline__ void count_uses(int nk)
+    {
+        uses0 += (uint32_t)((nk + 1) >> 1);
+        uses1 += (uint32_t)(nk >> 1);
+    }
+    __device__ __forceinline__ bool loads_this_tile() const { return !(PAIRED && full_tile) || wave < 4; }
+
+    __device__ __forceinline__ void arrive(int word, uint32_t n)
+    {
+        asm volatile("" ::: "memory");
+        if (lane == 0)
+            __hip_atomic_fetch_add(sflags + word, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        asm volatile("" ::: "memory");
+    }
+
+    // Bounded wait until word >= target (modulo 2^32). A wait that runs out
+    // (only a broken protocol could cause it) counts itself in the plan's stall
+    // counter and makes this wave stop waiting, so the kernel always ends.
+    __device__ __forceinline__ void wait_count(int word, uint32_t target)
+    {
+        asm volatile("" ::: "memory");
+        for (uint32_t i = 0; !broken; ++i) {
+            const uint32_t v = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(sflags + word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+            if ((int32_t)(v - target) >= 0)
+                break;
+            if (i == SPIN_LIMIT) {
+                broken = true;
+                if (lane == 0)
+                    __hip_atomic_fetch_add(stall_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+    }
+
+    // Flag form of stage_ready(kt): the loading waves wait for their own loads
+    // of kt, zero its k tail, and arrive on full; then every wave waits for the
+    // full count of this use.
+    __device__ __forceinline__ void stage_ready_flags(int kt, const TileCtx<C> &t)
+    {
+        const int s = kt & 1;
+        const uint32_t target = FLAG_UNIT * (use_of(kt) + 1);
+        if (loads_this_tile()) {
+            const uint32_t share = PAIRED && full_tile ? 2u : 1u;
+            if (sync == SYNC_MERGED && !is_tail(kt, t.k)) {
+                // A was issued before B (paired: own A, own B, partner A,
+                // partner B), so with B_LOADS younger loads left all A has landed
+                wait_vmcnt<C::B_LOADS>();
+                arrive(W_FULL + s, share);
+                wait_vmcnt<0>();
+                arrive(W_FULL_B + s, share);
+            } else {
+                wait_vmcnt<0>();
+                if (is_tail(kt, t.k))
+                    zero_k_tail(kt, s, t.k);
+                arrive(W_FULL + s, share);
+                if (sync == SYNC_MERGED)
+                    arrive(W_FULL_B + s, share);
+            }
+        }
+        wait_count(W_FULL + s, target);
+        if (sync == SYNC_MERGED)
+            wait_count(W_FULL_B + s, target);
+    }
+
+    // Every wave has issued its last read of k-tile kt's stage.
+    __device__ __forceinline__ void release_stage(int kt) { arrive(W_EMPTY + (kt & 1), 1u); }
+
+    // Before loading k-tile kt + 2 into kt's stage: every wave has released kt.
+    __device__ __forceinline__ void wait_stage_empty(int kt)
+    {
+        if (loads_this_tile())
+            wait_count(W_EMPTY + (kt & 1), FLAG_UNIT * (use_of(kt) + 1));
+    }
+
     // Wait for this wave's loads of k-tile kt, fix its k tail, then meet the
     // other waves: after this barrier every wave's loads of kt have landed and
     // every wave has finished reading the stage that k-tile kt + STAGES - 1
@@ -690,8 +795,14 @@ struct Mainloop {
             on_last_stage();
             return;
         }
+        // With stage flags the tile's first two fills need no empty wait: the
+        // previous tile's staging barrier came after every release.
+        const bool flags = sync != SYNC_BARRIER;
         issue_any(0, 0, t.k, nk);
-        stage_ready(0, t);
+        if (flags)
+            stage_ready_flags(0, t);
+        else
+            stage_ready(0, t);
         if (1 < nk)
             issue_any(1, 1, t.k, nk);
         if (nk == 1)
@@ -707,8 +818,16 @@ struct Mainloop {
                 else
                     rolling_step<0>(f, acc, stage, ks + 1);
             }
+            if (flags)
+                release_stage(kt);
             if (kt + 1 < nk) {
-                stage_ready(kt + 1, t);
+                if (flags) {
+                    stage_ready_flags(kt + 1, t);
+                    if (kt + 2 < nk)
+                        wait_stage_empty(kt);
+                } else {
+                    stage_ready(kt + 1, t);
+                }
                 if (kt + 2 < nk)
                     issue_any(kt + 2, stage, t.k, nk);
                 if (kt + 2 == nk)
@@ -718,6 +837,7 @@ struct Mainloop {
             // the last k-tile: a stage nobody writes any more; unused).
             rolling_step<(C::KSTEPS - 1) & 1>(f, acc, stage ^ 1, 0);
         }
+        count_uses(nk);
     }
 
     // ---- one wave per SIMD (16x16 blocks) ------------------------------------
@@ -1192,6 +1312,7 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     constexpr int SMEM_BYTES = C::LDS_BYTES > Epilogue<C>::LDS_BYTES ? C::LDS_BYTES : Epilogue<C>::LDS_BYTES;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
     __shared__ int32_t sched_slots[4];
+    __shared__ uint32_t stage_flags[6];
 
     const int tid = threadIdx.x;
     const int wave = uniform(tid >> 6);
@@ -1205,6 +1326,14 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     ml.wm = wave / C::WAVES_N;
     ml.wn = wave % C::WAVES_N;
     ml.setup_fragments();
+    ml.sflags = (__attribute__((address_space(3))) uint32_t *)stage_flags;
+    ml.stall_ctr = args->counters + CTR_SYNC_STALLS;
+    ml.sync = args->sync;
+    ml.uses0 = ml.uses1 = 0;
+    ml.broken = false;
+    if (tid < 6)
+        stage_flags[tid] = 0;
+    barrier_lds();
 
     TileScheduler sched{args->counters, args->total_tiles, args->num_workers, args->round, (int)blockIdx.x,
                         args->schedule, sched_slots, (int)(xcc_id_reg() % NUM_XCD), 0u};

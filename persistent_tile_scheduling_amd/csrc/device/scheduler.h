@@ -68,6 +68,7 @@ constexpr int CTR_CLAIM = 0;         // single device-wide claim counter
 constexpr int CTR_EXIT = 32;         // workers that have made their final claim
 constexpr int CTR_FINAL = 64;        // total claims of the last dynamic run
 constexpr int CTR_RUNS = 65;         // dynamic runs completed
+constexpr int CTR_SYNC_STALLS = 66;  // stage-flag waits that ran out (0 unless the hand-off is broken)
 constexpr int CTR_GATE = 96;         // scheduler probe: workers finished (late-worker gate)
 constexpr int CTR_XCD_STRIDE = 1024; // per-XCD claim counter x at CTR_XCD_STRIDE * (x + 1)
 constexpr int CTR_WORDS = CTR_XCD_STRIDE * (NUM_XCD + 1);

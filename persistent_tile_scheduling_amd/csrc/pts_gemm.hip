@@ -94,6 +94,7 @@ struct gemm_plan {
     int32_t dtype_d = GEMM_DTYPE_F32;
     int32_t schedule = GEMM_SCHEDULE_STATIC;
     int32_t round = 0;
+    int32_t sync = pts::SYNC_BARRIER;
     KernelEntry kernel{};
     int64_t total_tiles = 0;
     int32_t workers = 0;
@@ -147,8 +148,13 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
         return fail(GEMM_ERR_INVALID_VALUE, "the non-persistent schedule launches one workgroup per tile");
     if (desc->num_workers < 0)
         return fail(GEMM_ERR_INVALID_VALUE, "num_workers must be >= 0");
-    if (desc->flags != GEMM_FLAG_NONE)
-        return fail(GEMM_ERR_UNSUPPORTED, "unknown flags 0x%x", desc->flags);
+    if ((desc->flags & ~(GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED)) != 0 ||
+        desc->flags == (GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED))
+        return fail(GEMM_ERR_UNSUPPORTED, "unknown flags 0x%x (the two stage-flag layouts exclude each other)",
+                    desc->flags);
+    const int32_t sync = desc->flags == GEMM_FLAG_STAGE_FLAGS_FUSED    ? pts::SYNC_FUSED
+                         : desc->flags == GEMM_FLAG_STAGE_FLAGS_MERGED ? pts::SYNC_MERGED
+                                                                       : pts::SYNC_BARRIER;
     int tm = desc->tile_m == 0 ? 256 : desc->tile_m;
     int tn = desc->tile_n == 0 ? 256 : desc->tile_n;
     const bool out_bf16 = desc->dtype_d == GEMM_DTYPE_BF16;
@@ -169,6 +175,9 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
     if (entry == nullptr)
         return fail(GEMM_ERR_UNSUPPORTED, "tile %dx%d (k %d, %d stages, load path %d, %d waves, mfma %d) is not built",
                     tm, tn, desc->tile_k, desc->stages, desc->load_path, desc->waves, desc->mfma);
+    if (sync != pts::SYNC_BARRIER &&
+        !(entry->waves == 8 && entry->mfma == 16 && entry->stages == 2 && entry->load_path == pts::LOAD_DMA))
+        return fail(GEMM_ERR_UNSUPPORTED, "stage flags are built for the 8-wave 16x16 two-stage kernel only");
 
     auto plan = new (std::nothrow) gemm_plan();
     if (plan == nullptr)
@@ -259,6 +268,7 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
     plan->total_tiles = tiles;
     plan->workers = (int32_t)workers;
     plan->round = (int32_t)round;
+    plan->sync = sync;
 
     // counters first (4 KiB aligned blocks), then the group table
     const size_t cbytes = sizeof(uint32_t) * pts::CTR_WORDS;
@@ -327,12 +337,12 @@ gemm_status gemm_plan_set_trace(gemm_plan *plan, void *device_buf, size_t bytes)
     return GEMM_OK;
 }
 
-gemm_status gemm_plan_read_counters(const gemm_plan *plan, uint32_t out[4])
+gemm_status gemm_plan_read_counters(const gemm_plan *plan, uint32_t out[5])
 {
     if (plan == nullptr || out == nullptr)
         return fail(GEMM_ERR_INVALID_VALUE, "plan or out is NULL");
     hipError_t e = hipDeviceSynchronize();
-    uint32_t words[pts::CTR_RUNS + 1];
+    uint32_t words[pts::CTR_SYNC_STALLS + 1];
     if (e == hipSuccess)
         e = hipMemcpy(words, plan->d_counters, sizeof(words), hipMemcpyDeviceToHost);
     if (e != hipSuccess)
@@ -349,6 +359,7 @@ gemm_status gemm_plan_read_counters(const gemm_plan *plan, uint32_t out[4])
     out[1] = words[pts::CTR_EXIT];
     out[2] = words[pts::CTR_FINAL];
     out[3] = words[pts::CTR_RUNS];
+    out[4] = words[pts::CTR_SYNC_STALLS];
     return GEMM_OK;
 }
 
@@ -397,6 +408,7 @@ gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream)
     args.num_workers = plan->workers;
     args.schedule = plan->schedule;
     args.round = plan->round;
+    args.sync = plan->sync;
 
     void *kargs[] = {&args};
     e = hipLaunchKernel(plan->kernel.fn, dim3(plan->workers), dim3(plan->kernel.waves * 64), kargs, 0,

@@ -74,6 +74,7 @@ def check_counters(schedule, counters, tiles, workers):
     run takes tiles + workers claims. Per-XCD counters: a request may also fail
     on several XCD ranges before it finds a tile, so at least that many.
     """
+    assert counters[4] == 0, f"stage-flag waits ran out: {counters}"
     if schedule in ("static", "nonpersistent"):
         return
     assert counters[:2] == [0, 0], f"live counters not reset: {counters}"
@@ -83,12 +84,13 @@ def check_counters(schedule, counters, tiles, workers):
         assert tiles + workers <= counters[2] <= tiles + 8 * (tiles + workers), counters
 
 
-def run_single(m, n, k, a, b, out_dtype, schedule, tile=(0, 0), lda=0, ldb=0, ldd=0, num_workers=0, d=None):
+def run_single(m, n, k, a, b, out_dtype, schedule, tile=(0, 0), lda=0, ldb=0, ldd=0, num_workers=0, d=None,
+               flags=0):
     """One plan, one run; D defaults to a NaN-filled (m x ldd) buffer. ld = 0 is packed."""
     import persistent_tile_scheduling_amd as pts
     if d is None:
         d = torch.full((max(m, 1), max(ldd or n, 1)), float("nan"), dtype=out_dtype, device=DEV)
-    with pts.Plan([(m, n, k, lda, ldb, ldd)], out_dtype, tile, schedule, num_workers) as p:
+    with pts.Plan([(m, n, k, lda, ldb, ldd)], out_dtype, tile, schedule, num_workers, flags) as p:
         p.run([(a, b, d)])
         torch.cuda.synchronize()
         counters = p.counters()

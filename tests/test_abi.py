@@ -57,6 +57,10 @@ def test_status_strings(binding):
     (dict(schedule=3, num_workers=2), 1, "one workgroup per tile"),
     (dict(num_workers=-1), 1, "num_workers"),
     (dict(flags=0x80), 2, "flags"),
+    (dict(flags=3), 2, "exclude each other"),
+    (dict(flags=1, tile=(128, 128)), 2, "stage flags"),
+    (dict(flags=2, tile=(256, 256, 0, 0, 0, 4)), 2, "stage flags"),
+    (dict(flags=1, tile=(256, 256, 0, 0, 0, 8, 32)), 2, "stage flags"),
     (dict(tile=(96, 96)), 2, "not built"),
 ])
 def test_plan_create_rejects_bad_descriptors(binding, kwargs, status, fragment):
