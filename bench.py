@@ -102,6 +102,20 @@ class Concurrent:
             self.raw = None
 
 
+def copy_alone_ms(conc, runs):
+    """Median wall time of the concurrent copy by itself (synchronized per run)."""
+    import torch
+    ts = []
+    for _ in range(runs + 2):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        conc.launch()
+        torch.cuda.synchronize()
+        ts.append((time.perf_counter() - t0) * 1e3)
+    ts = sorted(ts[2:])
+    return ts[len(ts) // 2]
+
+
 def time_headline(pts, wl, ops, schedule, steps, warmup, conc=None):
     """K timed steps of one schedule, wall clock plus per-launch HIP events."""
     import torch
@@ -362,7 +376,16 @@ def main():
             r.update(tail_idle(pts, wl, ops, sched, conc))
             print(f"# trace {sched}: tail idle {r['tail_idle_frac']:.3f}, late start {r['late_start_frac']:.3f}",
                   file=sys.stderr, flush=True)
+    without_copy, copy_alone = None, None
     if conc is not None:
+        if len(schedules) > 1 and args.compare_rounds > 0:
+            # the same comparison with nothing else on the chip, and the copy on its own
+            without_copy = compare_schedules(pts, wl, ops, schedules, args.compare_rounds)
+            for sched, r in without_copy.items():
+                print(f"# without copy {sched}: median {r['kernel_ms_median']:.4f} ms, "
+                      f"{r['kernel_tflops_median']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+            copy_alone = copy_alone_ms(conc, 10)
+            print(f"# copy alone on {args.copy_cus} CUs: {copy_alone:.4f} ms", file=sys.stderr, flush=True)
         conc.close()
     vendor = vendor_gemm(wl, ops, args.steps) if args.vendor and len(wl["shapes"]) == 1 else None
     if vendor:
@@ -406,6 +429,11 @@ def main():
     if "static" in results and "kernel_ms_median" in results["static"]:
         line["dynamic_vs_static"] = {s: round(results["static"]["kernel_ms_median"] / r["kernel_ms_median"], 4)
                                      for s, r in results.items() if s != "static" and "kernel_ms_median" in r}
+    if without_copy:
+        line["without_copy"] = {s: {"kernel_ms_median": round(r["kernel_ms_median"], 5),
+                                    "kernel_tflops_median": round(r["kernel_tflops_median"], 2)}
+                                for s, r in without_copy.items()}
+        line["copy_alone_ms"] = round(copy_alone, 5)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)
