@@ -78,7 +78,7 @@ struct GemmArgs {
     int32_t num_workers;
     int32_t schedule;
     int32_t round;     // static dealing width (see static_position)
-    int32_t sync;      // stage hand-off: SYNC_BARRIER, SYNC_FUSED or SYNC_MERGED
+    int32_t pad;
     uint64_t d_vec_ok; // bit g: problem g's D rows allow vector stores
     const uint16_t *a[PTS_MAX_GROUPS];
     const uint16_t *b[PTS_MAX_GROUPS];
@@ -134,10 +134,13 @@ template <> struct Mfma<16> {
 // wave per SIMD (512 registers each); 2 x 4 gives two waves per SIMD (256
 // registers each), so one wave's LDS and memory waits overlap the other's
 // MFMAs. MB is the matrix instruction's output block edge (32 or 16).
+// SYNC is the stage hand-off (a compile-time choice, so the default barrier
+// form carries none of the counter code).
 template <int BM_, int BN_, int BK_, int STAGES_, bool OUT_BF16_, int LOAD_PATH_ = LOAD_DMA, int WAVES_M_ = 2,
-          int WAVES_N_ = 2, int MB_ = 32>
+          int WAVES_N_ = 2, int MB_ = 32, int SYNC_ = SYNC_BARRIER>
 struct GemmConfig {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+    static constexpr int SYNC = SYNC_;
     static constexpr bool OUT_BF16 = OUT_BF16_;
     static constexpr int LOAD_PATH = LOAD_PATH_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_, WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
@@ -612,7 +615,7 @@ struct Mainloop {
     static constexpr int W_FULL = 0, W_FULL_B = 2, W_EMPTY = 4; // word offsets (+ stage)
     __attribute__((address_space(3))) uint32_t *sflags;
     uint32_t *stall_ctr; // device counter of waits that ran out
-    int sync;
+    static constexpr int sync = C::SYNC;
     uint32_t uses0, uses1;
     bool broken; // a wait ran out: stop waiting (the plan's stall counter says the result is void)
 
@@ -797,7 +800,7 @@ struct Mainloop {
         }
         // With stage flags the tile's first two fills need no empty wait: the
         // previous tile's staging barrier came after every release.
-        const bool flags = sync != SYNC_BARRIER;
+        constexpr bool flags = C::SYNC != SYNC_BARRIER;
         issue_any(0, 0, t.k, nk);
         if (flags)
             stage_ready_flags(0, t);
@@ -1328,7 +1331,6 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     ml.setup_fragments();
     ml.sflags = (__attribute__((address_space(3))) uint32_t *)stage_flags;
     ml.stall_ctr = args->counters + CTR_SYNC_STALLS;
-    ml.sync = args->sync;
     ml.uses0 = ml.uses1 = 0;
     ml.broken = false;
     if (tid < 6)

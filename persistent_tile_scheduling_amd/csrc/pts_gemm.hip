@@ -43,15 +43,17 @@ struct KernelEntry {
     int load_path;
     int waves;
     int mfma;
+    int sync;
     const void *fn;
     int lds_bytes;
 };
 
-template <int BM, int BN, int BK, int S, bool BF16, int LP = pts::LOAD_DMA, int WM = 2, int WN = 2, int MB = 32>
+template <int BM, int BN, int BK, int S, bool BF16, int LP = pts::LOAD_DMA, int WM = 2, int WN = 2, int MB = 32,
+          int SYNC = pts::SYNC_BARRIER>
 KernelEntry make_entry()
 {
-    using C = pts::GemmConfig<BM, BN, BK, S, BF16, LP, WM, WN, MB>;
-    return KernelEntry{BM, BN, BK, S, BF16, LP, C::WAVES, MB, (const void *)&pts::gemm_persistent_kernel<C>,
+    using C = pts::GemmConfig<BM, BN, BK, S, BF16, LP, WM, WN, MB, SYNC>;
+    return KernelEntry{BM, BN, BK, S, BF16, LP, C::WAVES, MB, SYNC, (const void *)&pts::gemm_persistent_kernel<C>,
                        C::LDS_BYTES};
 }
 
@@ -79,6 +81,11 @@ const std::vector<KernelEntry> &kernel_table()
         make_entry<128, 128, 64, 2, true>(),  make_entry<128, 128, 64, 2, false>(),
         make_entry<128, 128, 32, 4, true>(),  make_entry<128, 128, 32, 4, false>(),
         make_entry<64, 64, 64, 2, true>(),    make_entry<64, 64, 64, 2, false>(),
+        // the default kernel with the stage hand-off through LDS arrive counters
+        make_entry<256, 256, 64, 2, true, pts::LOAD_DMA, 2, 4, 16, pts::SYNC_FUSED>(),
+        make_entry<256, 256, 64, 2, false, pts::LOAD_DMA, 2, 4, 16, pts::SYNC_FUSED>(),
+        make_entry<256, 256, 64, 2, true, pts::LOAD_DMA, 2, 4, 16, pts::SYNC_MERGED>(),
+        make_entry<256, 256, 64, 2, false, pts::LOAD_DMA, 2, 4, 16, pts::SYNC_MERGED>(),
     };
     return table;
 }
@@ -94,7 +101,6 @@ struct gemm_plan {
     int32_t dtype_d = GEMM_DTYPE_F32;
     int32_t schedule = GEMM_SCHEDULE_STATIC;
     int32_t round = 0;
-    int32_t sync = pts::SYNC_BARRIER;
     KernelEntry kernel{};
     int64_t total_tiles = 0;
     int32_t workers = 0;
@@ -168,16 +174,16 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
         if (e.bm == tm && e.bn == tn && e.out_bf16 == out_bf16 && (desc->tile_k == 0 || e.bk == desc->tile_k) &&
             (desc->stages == 0 || e.stages == desc->stages) &&
             (desc->load_path == 0 || e.load_path == desc->load_path - 1) &&
-            (desc->waves == 0 || e.waves == desc->waves) && (desc->mfma == 0 || e.mfma == desc->mfma)) {
+            (desc->waves == 0 || e.waves == desc->waves) && (desc->mfma == 0 || e.mfma == desc->mfma) &&
+            e.sync == sync) {
             entry = &e;
             break;
         }
+    if (entry == nullptr && sync != pts::SYNC_BARRIER)
+        return fail(GEMM_ERR_UNSUPPORTED, "stage flags are built for the 8-wave 16x16 two-stage 256x256 kernel only");
     if (entry == nullptr)
         return fail(GEMM_ERR_UNSUPPORTED, "tile %dx%d (k %d, %d stages, load path %d, %d waves, mfma %d) is not built",
                     tm, tn, desc->tile_k, desc->stages, desc->load_path, desc->waves, desc->mfma);
-    if (sync != pts::SYNC_BARRIER &&
-        !(entry->waves == 8 && entry->mfma == 16 && entry->stages == 2 && entry->load_path == pts::LOAD_DMA))
-        return fail(GEMM_ERR_UNSUPPORTED, "stage flags are built for the 8-wave 16x16 two-stage kernel only");
 
     auto plan = new (std::nothrow) gemm_plan();
     if (plan == nullptr)
@@ -268,7 +274,6 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
     plan->total_tiles = tiles;
     plan->workers = (int32_t)workers;
     plan->round = (int32_t)round;
-    plan->sync = sync;
 
     // counters first (4 KiB aligned blocks), then the group table
     const size_t cbytes = sizeof(uint32_t) * pts::CTR_WORDS;
@@ -408,7 +413,6 @@ gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream)
     args.num_workers = plan->workers;
     args.schedule = plan->schedule;
     args.round = plan->round;
-    args.sync = plan->sync;
 
     void *kargs[] = {&args};
     e = hipLaunchKernel(plan->kernel.fn, dim3(plan->workers), dim3(plan->kernel.waves * 64), kargs, 0,
