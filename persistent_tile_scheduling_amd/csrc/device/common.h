@@ -83,13 +83,15 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void *base)
 // vector-memory waits before the fragment reads of OTHER ring stages, which
 // serializes the prefetch. Here the kernel alone accounts for these loads
 // (explicit vmcnt waits before each stage is read). M0 carries the LDS
-// destination; the statement declares it clobbered.
+// destination. M0 is a reserved register the compiler sets itself before each
+// instruction of its own that reads it, so it is not named as clobbered (the
+// compiler warns that a reserved register in a clobber list is not honoured).
 __device__ __forceinline__ void dma_load16(uint32_t lds_addr, uint32_t voff, u32x4 rsrc, uint32_t soff)
 {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
                  : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 // The same load, performed only when `on` (a wave-uniform flag): with `on`
@@ -106,7 +108,7 @@ __device__ __forceinline__ void dma_load16_if(uint32_t lds_addr, uint32_t voff, 
                  "buffer_load_dwordx4 %2, %3, %4 offen lds\n\ts_mov_b64 exec, %0"
                  : "=&s"(saved)
                  : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(0u), "s"(mask)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_address(const void *p)

@@ -1238,7 +1238,8 @@ __device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const typena
 {
     using E = Epilogue<C>;
     const int lr = lane % C::MB, lc = (lane / C::MB) * 4;
-    constexpr int QS = C::MB / 8; // 4-element groups per lane per block
+    constexpr int QS = C::MB * C::MB / 256; // 4-element groups per lane per block
+    static_assert(sizeof(typename C::Acc) == QS * 16, "accumulator groups");
     uint8_t *const tile_base = (uint8_t *)t.d + ((int64_t)t.row0 * t.ldd + t.col0) * E::ES;
 #pragma unroll
     for (int pass = 0; pass < E::PASSES; ++pass) {
