@@ -1225,6 +1225,8 @@ struct Epilogue {
     static constexpr int MI_PASS = C::MI / PASSES;
     static constexpr int CHUNKS_ROW = C::BN / 4;             // 4-element groups per row
     static constexpr int LDS_BYTES = PASS_ROWS * PITCH;
+    static constexpr int ITERS = PASS_ROWS * CHUNKS_ROW / C::THREADS; // groups per thread per pass
+    static constexpr int BATCH = ITERS < 4 ? ITERS : 4; // staged groups read ahead of their stores
     static_assert(C::MI % PASSES == 0, "passes split the wave's row blocks");
     static_assert(LDS_BYTES <= 150 * 1024, "epilogue staging must fit LDS");
 };
@@ -1241,6 +1243,9 @@ __device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const typena
     constexpr int QS = C::MB * C::MB / 256; // 4-element groups per lane per block
     static_assert(sizeof(typename C::Acc) == QS * 16, "accumulator groups");
     uint8_t *const tile_base = (uint8_t *)t.d + ((int64_t)t.row0 * t.ldd + t.col0) * E::ES;
+    // (one wave per SIMD only: with two waves per SIMD the batched form came out
+    // slower, its extra registers spilling around the tile loop)
+    const bool full = C::WAVES == 4 && C::LOAD_PATH == LOAD_DMA && t.vec_ok && t.vm == C::BM && t.vn == C::BN;
 #pragma unroll
     for (int pass = 0; pass < E::PASSES; ++pass) {
         // accumulators of this pass's row blocks -> LDS
@@ -1265,6 +1270,45 @@ __device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const typena
         barrier_lds();
         // LDS -> D, one 4-element group per lane per step
         constexpr int TOTAL = E::PASS_ROWS * E::CHUNKS_ROW;
+        if (full) {
+            // Full tile, vector-store rows: no masks, and the staged reads go
+            // out BATCH at a time ahead of their conversions and stores, so
+            // the LDS latency is paid once per batch instead of once per group
+            // (with one wave per SIMD nothing else hides it).
+            static_assert(TOTAL == E::ITERS * C::THREADS && E::ITERS % E::BATCH == 0, "store batches");
+#pragma unroll
+            for (int it0 = 0; it0 < TOTAL / C::THREADS; it0 += E::BATCH) {
+                f32x4 v32[E::BATCH];
+#pragma unroll
+                for (int b = 0; b < E::BATCH; ++b) {
+                    const int idx = tid + (it0 + b) * C::THREADS;
+                    v32[b] = *(const f32x4 *)(smem + (idx / E::CHUNKS_ROW) * E::PITCH + (idx % E::CHUNKS_ROW) * 16);
+                }
+#pragma unroll
+                for (int b = 0; b < E::BATCH; ++b) {
+                    const int idx = tid + (it0 + b) * C::THREADS;
+                    const int sr = idx / E::CHUNKS_ROW;
+                    const int c = (idx % E::CHUNKS_ROW) * 4;
+                    // opaque: formed here, not hoisted into registers held across the passes
+                    const int i = (int)opaque_v(
+                        (uint32_t)((sr / E::WAVE_ROWS) * C::WTM + pass * E::WAVE_ROWS + (sr % E::WAVE_ROWS)));
+                    uint8_t *dst = tile_base + ((int64_t)i * t.ldd + c) * E::ES;
+                    if constexpr (C::OUT_BF16) {
+                        bf16x4 v;
+                        v[0] = (__bf16)v32[b][0];
+                        v[1] = (__bf16)v32[b][1];
+                        v[2] = (__bf16)v32[b][2];
+                        v[3] = (__bf16)v32[b][3];
+                        *(bf16x4 *)dst = v;
+                    } else {
+                        *(f32x4 *)dst = v32[b];
+                    }
+                }
+            }
+            if (pass + 1 < E::PASSES)
+                barrier_lds();
+            continue;
+        }
 #pragma unroll 2
         for (int idx = tid; idx < TOTAL; idx += C::THREADS) {
             const int sr = idx / E::CHUNKS_ROW;
