@@ -315,6 +315,8 @@ def main():
     ap.add_argument("--load-path", type=int, default=0, help="1 = global->LDS, 2 = via registers (0 = default)")
     ap.add_argument("--waves", type=int, default=0, help="waves per workgroup, 4 or 8 (0 = default)")
     ap.add_argument("--mfma", type=int, default=0, help="MFMA block edge, 16 or 32 (0 = default)")
+    ap.add_argument("--problem-order", default="deepest_first", choices=["deepest_first", "as_given"],
+                    help="tile order of grouped problems: deepest first (default) or as given")
     ap.add_argument("--stage-sync", default="barrier", choices=["barrier", "fused", "merged"],
                     help="stage hand-off: workgroup barrier, or LDS full/empty counters (2 or 3 words per stage)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
@@ -345,6 +347,8 @@ def main():
     wl["tile"] = tuple(wl["tile"][:2]) + (args.tile_k, args.stages, args.load_path, args.waves, args.mfma)
     wl["flags"] = {"barrier": 0, "fused": pts.GEMM_FLAG_STAGE_FLAGS_FUSED,
                    "merged": pts.GEMM_FLAG_STAGE_FLAGS_MERGED}[args.stage_sync]
+    if args.problem_order == "as_given":
+        wl["flags"] |= pts.GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN
     print(f"# workload {args.workload}: {wl['desc']}", file=sys.stderr, flush=True)
     ops = make_operands(wl)
     conc = Concurrent(pts, wl["copy"], args.copy_cus) if wl["copy"] else None
@@ -407,7 +411,8 @@ def main():
         "config": {"workload": wl["desc"], "schedule": head_sched,
                    "shapes": wl["shapes"] if len(wl["shapes"]) <= 4 else f"{len(wl['shapes'])} problems",
                    "tile": list(wl["tile"]), "out_dtype": str(wl["out"]).replace("torch.", ""),
-                   "copy_cus": args.copy_cus if wl["copy"] else None, "stage_sync": args.stage_sync},
+                   "copy_cus": args.copy_cus if wl["copy"] else None, "stage_sync": args.stage_sync,
+                   "problem_order": args.problem_order},
         "roofline": {"bound": "mfma", "achieved": round(head["kernel_tflops"], 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(head["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),

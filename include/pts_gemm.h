@@ -115,6 +115,16 @@ typedef struct {
  */
 #define GEMM_FLAG_STAGE_FLAGS_FUSED 1u
 #define GEMM_FLAG_STAGE_FLAGS_MERGED 2u
+/*
+ * Tile order of a grouped plan. By default the problems are laid out in the
+ * tile space deepest first (descending number of k-tiles, ties in descriptor
+ * order), so the costliest tiles are taken first and the cheap ones fill the
+ * end of the run, whatever the schedule. With this flag the problems keep the
+ * descriptor's order (the offsets-array order of the "Schedules" page,
+ * section "Dynamic Domain"). Only the tile order changes: every tile is
+ * computed once either way, traces report the descriptor's problem index.
+ */
+#define GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN 4u
 
 typedef struct {
     int32_t group_count;       /* 1 = one GEMM; 2..GEMM_MAX_GROUPS = grouped, one launch */
@@ -199,8 +209,10 @@ gemm_status gemm_plan_query(const gemm_plan *plan, int64_t *num_tiles, int32_t *
  *   struct { uint64 t_start, t_end; int32 tiles, worker; uint32 hw_id, xcc_id; }
  *                                                  -- 32 bytes, at index `worker`
  *
- * `tile` is the tile's position in the plan's tile order (problems in turn;
- * inside a problem, groups of 8 tile rows walked column by column), `claim`
+ * `tile` is the tile's position in the plan's tile order (problems in turn,
+ * deepest first unless GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN; inside a problem,
+ * groups of 8 tile rows walked column by column), `group` the problem's index
+ * in the descriptor, `claim`
  * the scheduler's value that selected it (static: the logical grid-stride
  * index; dynamic: the counter value; per-XCD: XCD * 2^24 + counter value v,
  * i.e. logical index XCD + 8 v).

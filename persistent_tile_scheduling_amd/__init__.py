@@ -38,6 +38,7 @@ GEMM_MAX_GROUPS = 64
 GEMM_FLAG_NONE = 0
 GEMM_FLAG_STAGE_FLAGS_FUSED = 1
 GEMM_FLAG_STAGE_FLAGS_MERGED = 2
+GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN = 4
 
 TILE_TRACE_BYTES = 56
 WORKER_TRACE_BYTES = 32

@@ -49,7 +49,8 @@ struct GroupDesc {
     int32_t tiles_n;     // ceil(n / BN)
     int32_t tile_begin;  // index of the problem's first tile in the run's tile space
     int32_t num_k_tiles; // ceil(k / BK)
-    int32_t pad0, pad1;
+    int32_t index;       // the problem's index in the plan descriptor (tile order may differ)
+    int32_t pad1;
     int64_t lda, ldb, ldd;
 };
 
@@ -209,7 +210,8 @@ __device__ __forceinline__ void wait_stage_loads(int younger)
 
 template <class C>
 struct TileCtx {
-    int group;
+    int group;     // index in the plan's tile order (selects the operand pointers)
+    int problem;   // index in the plan descriptor
     int row0, col0, vm, vn; // tile origin and valid extent
     int k, nk;
     int kt0; // first k-tile of the tile's k order (see k_phase)
@@ -298,6 +300,7 @@ __device__ __forceinline__ TileCtx<C> decode_tile(KernArgs args, int t, int grou
     raster_tile(local, (gd.m + C::BM - 1) / C::BM, gd.tiles_n, tm, tn);
     TileCtx<C> c;
     c.group = g;
+    c.problem = gp->index;
     c.row0 = tm * C::BM;
     c.col0 = tn * C::BN;
     c.vm = min(C::BM, gd.m - c.row0);
@@ -1421,7 +1424,7 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
             r.claim = cur.claim;
             r.worker = blockIdx.x;
             r.seq = seq;
-            r.group = tc.group;
+            r.group = tc.problem;
             r.row0 = tc.row0;
             r.col0 = tc.col0;
             r.xcc_id = xcc_id_reg();

@@ -97,7 +97,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct gemm_plan {
     int device = 0;
     int32_t group_count = 0;
-    std::vector<gemm_shape> shapes; // ld values resolved
+    std::vector<gemm_shape> shapes; // ld values resolved, in tile order
+    std::vector<int32_t> order;     // tile-order slot -> descriptor problem index
     int32_t dtype_d = GEMM_DTYPE_F32;
     int32_t schedule = GEMM_SCHEDULE_STATIC;
     int32_t round = 0;
@@ -154,13 +155,17 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
         return fail(GEMM_ERR_INVALID_VALUE, "the non-persistent schedule launches one workgroup per tile");
     if (desc->num_workers < 0)
         return fail(GEMM_ERR_INVALID_VALUE, "num_workers must be >= 0");
-    if ((desc->flags & ~(GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED)) != 0 ||
+    if ((desc->flags & ~(GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED |
+                         GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN)) != 0 ||
         desc->flags == (GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED))
         return fail(GEMM_ERR_UNSUPPORTED, "unknown flags 0x%x (the two stage-flag layouts exclude each other)",
                     desc->flags);
-    const int32_t sync = desc->flags == GEMM_FLAG_STAGE_FLAGS_FUSED    ? pts::SYNC_FUSED
-                         : desc->flags == GEMM_FLAG_STAGE_FLAGS_MERGED ? pts::SYNC_MERGED
-                                                                       : pts::SYNC_BARRIER;
+    const uint32_t sync_flags = desc->flags & (GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED);
+    if (sync_flags == (GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED))
+        return fail(GEMM_ERR_UNSUPPORTED, "flags 0x%x: the two stage-flag layouts exclude each other", desc->flags);
+    const int32_t sync = sync_flags == GEMM_FLAG_STAGE_FLAGS_FUSED    ? pts::SYNC_FUSED
+                         : sync_flags == GEMM_FLAG_STAGE_FLAGS_MERGED ? pts::SYNC_MERGED
+                                                                      : pts::SYNC_BARRIER;
     int tm = desc->tile_m == 0 ? 256 : desc->tile_m;
     int tn = desc->tile_n == 0 ? 256 : desc->tile_n;
     const bool out_bf16 = desc->dtype_d == GEMM_DTYPE_BF16;
@@ -189,6 +194,7 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
     if (plan == nullptr)
         return fail(GEMM_ERR_OUT_OF_MEMORY, "host allocation failed");
     std::vector<pts::GroupDesc> groups(desc->group_count);
+    std::vector<gemm_shape> shapes(desc->group_count);
     int64_t tiles = 0;
     for (int g = 0; g < desc->group_count; ++g) {
         gemm_shape s = desc->shapes[g];
@@ -215,7 +221,7 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
             delete plan;
             return fail(GEMM_ERR_UNSUPPORTED, "problem %d: lda/ldb too large for 32-bit tile offsets", g);
         }
-        plan->shapes.push_back(s);
+        shapes[g] = s;
         pts::GroupDesc &gd = groups[g];
         gd.m = (int32_t)s.m;
         gd.n = (int32_t)s.n;
@@ -223,7 +229,8 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
         gd.tiles_n = (int32_t)ceil_div(s.n, tn);
         gd.tile_begin = (int32_t)tiles;
         gd.num_k_tiles = (int32_t)ceil_div(s.k, entry->bk);
-        gd.pad0 = gd.pad1 = 0;
+        gd.index = g;
+        gd.pad1 = 0;
         gd.lda = s.lda;
         gd.ldb = s.ldb;
         gd.ldd = s.ldd;
@@ -234,6 +241,30 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
             return fail(GEMM_ERR_UNSUPPORTED, "more than 2^27 output tiles");
         }
     }
+    // Tile order: deepest problems first (a tile's cost grows with its
+    // k-tiles), so the long tiles start early and the short ones fill the end
+    // of the run; the descriptor's order on request. Positions are then
+    // re-counted in that order.
+    std::vector<int32_t> order(desc->group_count);
+    for (int g = 0; g < desc->group_count; ++g)
+        order[g] = g;
+    if ((desc->flags & GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN) == 0)
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int32_t x, int32_t y) { return groups[x].num_k_tiles > groups[y].num_k_tiles; });
+    {
+        std::vector<pts::GroupDesc> sorted(desc->group_count);
+        int64_t begin = 0;
+        for (int i = 0; i < desc->group_count; ++i) {
+            sorted[i] = groups[order[i]];
+            sorted[i].tile_begin = (int32_t)begin;
+            const gemm_shape &s = shapes[order[i]];
+            if (s.m > 0 && s.n > 0)
+                begin += ceil_div(s.m, tm) * ceil_div(s.n, tn);
+            plan->shapes.push_back(s);
+        }
+        groups.swap(sorted);
+    }
+    plan->order = order;
 
     hipError_t e = hipGetDevice(&plan->device);
     if (e != hipSuccess) {
@@ -385,16 +416,18 @@ gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream)
     memset(&args, 0, sizeof args);
     const size_t esize_d = plan->dtype_d == GEMM_DTYPE_BF16 ? 2 : 4;
     for (int g = 0; g < plan->group_count; ++g) {
+        // slot g of the tile order holds descriptor problem p
+        const int p = plan->order[g];
         const gemm_shape &s = plan->shapes[g];
-        const gemm_operands &o = ops[g];
+        const gemm_operands &o = ops[p];
         const bool has_tiles = s.m > 0 && s.n > 0;
         if (has_tiles) {
             if (o.d == nullptr || (s.k > 0 && (o.a == nullptr || o.b == nullptr)))
-                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: NULL operand pointer", g);
+                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: NULL operand pointer", p);
             if (s.k > 0 && (((uintptr_t)o.a % 16) != 0 || ((uintptr_t)o.b % 16) != 0))
-                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: A and B must be 16-byte aligned", g);
+                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: A and B must be 16-byte aligned", p);
             if (((uintptr_t)o.d % esize_d) != 0)
-                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: D must be element aligned", g);
+                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: D must be element aligned", p);
         }
         args.a[g] = (const uint16_t *)o.a;
         args.b[g] = (const uint16_t *)o.b;

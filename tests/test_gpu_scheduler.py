@@ -23,6 +23,7 @@ import pytest
 import torch
 
 import oracle
+import pts_inputs as gen
 from tests import gpu_util as U
 
 pytestmark = pytest.mark.gpu
@@ -220,3 +221,38 @@ def test_copy_kernel(pts):
         torch.cuda.synchronize()
         assert torch.equal(dst[:n], src)
         assert torch.all(dst[n:] == 1234)
+
+
+@pytest.mark.parametrize("as_given", [False, True])
+@pytest.mark.parametrize("schedule", ["static", "dynamic", "dynamic_xcd"])
+def test_grouped_tile_order_deepest_first(pts, schedule, as_given):
+    # problems of different depth: by default the deepest come first in the tile
+    # order (so they are dealt / claimed first); on request the descriptor order
+    ks = [64, 1000, 8, 520, 1000, 136]
+    shapes = [(300, 500, k) for k in ks]
+    flags = pts.GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN if as_given else 0
+    tensors, refs = [], []
+    for g, (m, n, k) in enumerate(shapes):
+        a_bits = gen.operand_a(m, k, 7, tensor_id=16 + 2 * g, kind="integer")
+        b_bits = gen.operand_b(k, n, 7, tensor_id=17 + 2 * g, kind="integer")
+        refs.append(oracle.gemm(a_bits, b_bits, m, n, k))
+        tensors.append((U.bits_to_device(a_bits), U.bits_to_device(b_bits),
+                        torch.full((m, n), float("nan"), dtype=torch.float32, device=U.DEV)))
+    with pts.Plan(shapes, torch.float32, (256, 256), schedule, 0, flags) as p:
+        buf = torch.zeros(p.trace_bytes() // 4 + 4, dtype=torch.int32, device=U.DEV)
+        p.set_trace(buf)
+        p.run(tensors)
+        torch.cuda.synchronize()
+        tiles, _ = pts.decode_trace(buf, p.num_tiles, p.num_workers)
+        U.check_counters(schedule, p.counters(), p.num_tiles, p.num_workers)
+    for g, ((_, _, d), ref) in enumerate(zip(tensors, refs)):
+        U.check_exact(d, ref, f"problem {g} {schedule}")
+    # every tile once, reported under its descriptor index
+    want = sorted((g, r0, c0) for (g, r0, c0, _, _) in oracle.tile_coords([s[:2] for s in shapes], 256, 256))
+    got = sorted(zip(tiles["group"].tolist(), tiles["row0"].tolist(), tiles["col0"].tolist()))
+    assert got == want
+    # problem of each position, in position order
+    by_pos = [int(g) for _, g in sorted(zip(tiles["tile"].tolist(), tiles["group"].tolist()))]
+    per_problem = 2 * 2   # 300 x 500 in 256 x 256 tiles
+    order = list(range(len(ks))) if as_given else sorted(range(len(ks)), key=lambda g: -((ks[g] + 63) // 64))
+    assert by_pos == [g for g in order for _ in range(per_problem)]
