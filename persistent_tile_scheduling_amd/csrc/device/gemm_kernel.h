@@ -791,6 +791,28 @@ struct Mainloop {
         }
     }
 
+    // The loads and stage barriers of run_burst_rolling without its fragment
+    // reads and MFMAs (same calls in the same order, so every wave meets the
+    // same barriers).
+    template <class Hook>
+    __device__ __forceinline__ void run_rolling_idle(const TileCtx<C> &t, Hook &on_last_stage)
+    {
+        const int nk = t.nk;
+        issue_any(0, 0, t.k, nk);
+        stage_ready(0, t);
+        if (1 < nk)
+            issue_any(1, 1, t.k, nk);
+        if (nk == 1)
+            on_last_stage();
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+            stage_ready(kt + 1, t);
+            if (kt + 2 < nk)
+                issue_any(kt + 2, kt & 1, t.k, nk);
+            if (kt + 2 == nk)
+                on_last_stage();
+        }
+    }
+
     template <class Hook>
     __device__ __forceinline__ void run_burst_rolling(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI],
                                                       Hook &on_last_stage)
@@ -800,6 +822,16 @@ struct Mainloop {
         if (nk == 0) {
             on_last_stage();
             return;
+        }
+        if constexpr (C::SYNC == SYNC_BARRIER) {
+            // A wave whose whole wave tile lies outside the valid rows or
+            // columns of an edge tile computes nothing: it only loads and meets
+            // the stage barriers, so edge tiles really are cheaper (its partner
+            // on the SIMD gets the matrix unit to itself).
+            if (wm * C::WTM >= t.vm || wn * C::WTN >= t.vn) {
+                run_rolling_idle(t, on_last_stage);
+                return;
+            }
         }
         // With stage flags the tile's first two fills need no empty wait: the
         // previous tile's staging barrier came after every release.
