@@ -614,8 +614,11 @@ struct Mainloop {
     // performed in order, so an arrive issued after a wave's reads (or after its
     // load wait) is seen only after them.
     static constexpr uint32_t FLAG_UNIT = C::WAVES;
-    static constexpr uint32_t SPIN_LIMIT = 1u << 15; // ~2M cycles: far beyond any legitimate wait
-    static constexpr int W_FULL = 0, W_FULL_B = 2, W_EMPTY = 4; // word offsets (+ stage)
+    // polls of a bounded wait: with the sleep and the LDS round trip each, a few
+    // million cycles (milliseconds), far beyond any legitimate wait
+    static constexpr uint32_t SPIN_LIMIT = 1u << 15;
+    // word offsets (+ stage); the fused layout uses the full and empty words only
+    static constexpr int W_FULL = 0, W_FULL_B = 2, W_EMPTY = 4;
     __attribute__((address_space(3))) uint32_t *sflags;
     uint32_t *stall_ctr; // device counter of waits that ran out
     static constexpr int sync = C::SYNC;
