@@ -125,6 +125,13 @@ typedef struct {
  * computed once either way, traces report the descriptor's problem index.
  */
 #define GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN 4u
+/*
+ * Test only, with a stage-flag layout: every wait for a full counter asks for
+ * one arrival more than can ever come, so every such wait runs out. Each wave
+ * counts its first expired wait in out[4] of gemm_plan_read_counters and waits
+ * no more; the kernel ends and D is void. It shows that the waits are bounded.
+ */
+#define GEMM_FLAG_DEBUG_STAGE_FLAG_STALL 8u
 
 typedef struct {
     int32_t group_count;       /* 1 = one GEMM; 2..GEMM_MAX_GROUPS = grouped, one launch */

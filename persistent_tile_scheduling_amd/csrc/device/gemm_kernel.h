@@ -79,7 +79,7 @@ struct GemmArgs {
     int32_t num_workers;
     int32_t schedule;
     int32_t round;     // static dealing width (see static_position)
-    int32_t pad;
+    int32_t full_excess; // test only: added to every stage-flag full target (0 in normal runs)
     uint64_t d_vec_ok; // bit g: problem g's D rows allow vector stores
     const uint16_t *a[PTS_MAX_GROUPS];
     const uint16_t *b[PTS_MAX_GROUPS];
@@ -623,6 +623,7 @@ struct Mainloop {
     uint32_t *stall_ctr; // device counter of waits that ran out
     static constexpr int sync = C::SYNC;
     uint32_t uses0, uses1;
+    uint32_t full_excess; // added to every full target; nonzero only to test the bounded wait
     bool broken; // a wait ran out: stop waiting (the plan's stall counter says the result is void)
 
     __device__ __forceinline__ uint32_t use_of(int kt) const { return ((kt & 1) ? uses1 : uses0) + (uint32_t)(kt >> 1); }
@@ -669,7 +670,7 @@ struct Mainloop {
     __device__ __forceinline__ void stage_ready_flags(int kt, const TileCtx<C> &t)
     {
         const int s = kt & 1;
-        const uint32_t target = FLAG_UNIT * (use_of(kt) + 1);
+        const uint32_t target = FLAG_UNIT * (use_of(kt) + 1) + full_excess;
         if (loads_this_tile()) {
             const uint32_t share = PAIRED && full_tile ? 2u : 1u;
             if (sync == SYNC_MERGED && !is_tail(kt, t.k)) {
@@ -1415,6 +1416,7 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     ml.sflags = (__attribute__((address_space(3))) uint32_t *)stage_flags;
     ml.stall_ctr = args->counters + CTR_SYNC_STALLS;
     ml.uses0 = ml.uses1 = 0;
+    ml.full_excess = C::SYNC != SYNC_BARRIER ? (uint32_t)args->full_excess : 0u;
     ml.broken = false;
     if (tid < 6)
         stage_flags[tid] = 0;

@@ -102,6 +102,7 @@ struct gemm_plan {
     int32_t dtype_d = GEMM_DTYPE_F32;
     int32_t schedule = GEMM_SCHEDULE_STATIC;
     int32_t round = 0;
+    int32_t full_excess = 0; // test only (GEMM_FLAG_DEBUG_STAGE_FLAG_STALL)
     KernelEntry kernel{};
     int64_t total_tiles = 0;
     int32_t workers = 0;
@@ -156,7 +157,7 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
     if (desc->num_workers < 0)
         return fail(GEMM_ERR_INVALID_VALUE, "num_workers must be >= 0");
     if ((desc->flags & ~(GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED |
-                         GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN)) != 0 ||
+                         GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN | GEMM_FLAG_DEBUG_STAGE_FLAG_STALL)) != 0 ||
         desc->flags == (GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED))
         return fail(GEMM_ERR_UNSUPPORTED, "unknown flags 0x%x (the two stage-flag layouts exclude each other)",
                     desc->flags);
@@ -166,6 +167,8 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
     const int32_t sync = sync_flags == GEMM_FLAG_STAGE_FLAGS_FUSED    ? pts::SYNC_FUSED
                          : sync_flags == GEMM_FLAG_STAGE_FLAGS_MERGED ? pts::SYNC_MERGED
                                                                       : pts::SYNC_BARRIER;
+    if ((desc->flags & GEMM_FLAG_DEBUG_STAGE_FLAG_STALL) != 0 && sync == pts::SYNC_BARRIER)
+        return fail(GEMM_ERR_INVALID_VALUE, "the stall test flag needs a stage-flag layout");
     int tm = desc->tile_m == 0 ? 256 : desc->tile_m;
     int tn = desc->tile_n == 0 ? 256 : desc->tile_n;
     const bool out_bf16 = desc->dtype_d == GEMM_DTYPE_BF16;
@@ -305,6 +308,7 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
     plan->total_tiles = tiles;
     plan->workers = (int32_t)workers;
     plan->round = (int32_t)round;
+    plan->full_excess = (desc->flags & GEMM_FLAG_DEBUG_STAGE_FLAG_STALL) != 0 ? 1 : 0;
 
     // counters first (4 KiB aligned blocks), then the group table
     const size_t cbytes = sizeof(uint32_t) * pts::CTR_WORDS;
@@ -446,6 +450,7 @@ gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream)
     args.num_workers = plan->workers;
     args.schedule = plan->schedule;
     args.round = plan->round;
+    args.full_excess = plan->full_excess;
 
     void *kargs[] = {&args};
     e = hipLaunchKernel(plan->kernel.fn, dim3(plan->workers), dim3(plan->kernel.waves * 64), kargs, 0,

@@ -61,6 +61,7 @@ def test_status_strings(binding):
     (dict(flags=1, tile=(128, 128)), 2, "stage flags"),
     (dict(flags=2, tile=(256, 256, 0, 0, 0, 4)), 2, "stage flags"),
     (dict(flags=1, tile=(256, 256, 0, 0, 0, 8, 32)), 2, "stage flags"),
+    (dict(flags=8), 1, "stall test flag"),
     (dict(tile=(96, 96)), 2, "not built"),
 ])
 def test_plan_create_rejects_bad_descriptors(binding, kwargs, status, fragment):

@@ -103,3 +103,32 @@ def test_grouped_variable_k(pts, mode):
             U.check_counters(sched, counters, p.num_tiles, p.num_workers)
         for (m, n, k), (_, _, d), ref in zip(problems, tensors, refs):
             U.check_exact(d, ref, f"grouped {mode} {(m, n, k)} {sched}")
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_waits_are_bounded(pts, mode):
+    # Forced from the host: every full target asks for one arrival too many, so
+    # every wave's first wait runs out. The kernel must still end, promptly, with
+    # one expired wait counted per wave; a normal plan afterwards runs clean.
+    import time
+    m = n = k = 512
+    a = torch.zeros((m, k), dtype=torch.bfloat16, device=U.DEV)
+    b = torch.zeros((n, k), dtype=torch.bfloat16, device=U.DEV)
+    d = torch.empty((m, n), dtype=torch.float32, device=U.DEV)
+    U.log(f"bounded stage-flag waits {mode}")
+    flags = MODES[mode] | pts.GEMM_FLAG_DEBUG_STAGE_FLAG_STALL
+    with pts.Plan([(m, n, k)], torch.float32, DEFAULT, "static", 0, flags) as p:
+        t0 = time.perf_counter()
+        p.run([(a, b, d)])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        counters = p.counters()
+        waves = p.num_workers * 8
+    assert counters[4] == waves, counters
+    assert elapsed < 5.0, elapsed
+    d.fill_(float("nan"))
+    with pts.Plan([(m, n, k)], torch.float32, DEFAULT, "static", 0, MODES[mode]) as p:
+        p.run([(a, b, d)])
+        torch.cuda.synchronize()
+        assert p.counters()[4] == 0
+    assert torch.count_nonzero(d).item() == 0
