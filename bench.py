@@ -326,6 +326,8 @@ def main():
                     help="interleaved rounds of every schedule for the comparison (0 = skip)")
     ap.add_argument("--no-vendor", dest="vendor", action="store_false",
                     help="skip the vendor BLAS context timing")
+    ap.add_argument("--vendor-only", action="store_true",
+                    help="time only the vendor BLAS on the workload's operands (for side-by-side profiles)")
     ap.add_argument("--copy-cus", type=int, default=64,
                     help="compute units the concurrent copy may use (0 = all, unmasked stream)")
     ap.add_argument("--calibration-copy", type=int, default=0,
@@ -351,6 +353,13 @@ def main():
         wl["flags"] |= pts.GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN
     print(f"# workload {args.workload}: {wl['desc']}", file=sys.stderr, flush=True)
     ops = make_operands(wl)
+    if args.vendor_only:
+        vendor = vendor_gemm(wl, ops, args.steps) if len(wl["shapes"]) == 1 else None
+        if vendor is None:
+            print("--vendor-only needs a single-problem workload with bf16 output", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"vendor_library": vendor, "config": {"workload": wl["desc"]}}), flush=True)
+        return
     conc = Concurrent(pts, wl["copy"], args.copy_cus) if wl["copy"] else None
     torch.cuda.synchronize()
 
