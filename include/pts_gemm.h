@@ -193,7 +193,11 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan);
  * Returns GEMM_ERR_INVALID_VALUE for a NULL or misaligned pointer (nothing is
  * launched), GEMM_ERR_HIP if the launch fails. Problems with m = 0 or n = 0
  * write nothing; k = 0 writes zeros. The run must be on the device the plan
- * was created on.
+ * was created on. The call enqueues that one kernel and nothing else (no
+ * memset, copy or host synchronisation; the dynamic schedules' claim counters
+ * are put back to zero by the kernel at the end of each run), so it may be
+ * recorded into a HIP graph by stream capture and replayed; the operand
+ * pointers are then fixed at capture time.
  */
 gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream);
 
