@@ -1253,6 +1253,9 @@ struct Mainloop {
 // one instruction fall in distinct LDS banks.
 // Only rows < M and columns < N of the problem are written ("Schedules" page,
 // section "Domains": an index is stored only while it is in range).
+// D is written once and never read back by the kernel, so its vector stores
+// are non-temporal: they do not displace the A and B lines that the tiles in
+// flight on the same die still share in its L2.
 template <class C>
 struct Epilogue {
     static constexpr int ES = C::OUT_BF16 ? 2 : 4;   // bytes per element of D
@@ -1338,9 +1341,9 @@ __device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const typena
                         v[1] = (__bf16)v32[b][1];
                         v[2] = (__bf16)v32[b][2];
                         v[3] = (__bf16)v32[b][3];
-                        *(bf16x4 *)dst = v;
+                        __builtin_nontemporal_store(v, (bf16x4 *)dst);
                     } else {
-                        *(f32x4 *)dst = v32[b];
+                        __builtin_nontemporal_store(v32[b], (f32x4 *)dst);
                     }
                 }
             }
@@ -1365,7 +1368,7 @@ __device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const typena
                 v[2] = (__bf16)v32[2];
                 v[3] = (__bf16)v32[3];
                 if (t.vec_ok && c + 3 < t.vn) {
-                    *(bf16x4 *)dst = v;
+                    __builtin_nontemporal_store(v, (bf16x4 *)dst);
                 } else {
                     for (int e = 0; e < 4 && c + e < t.vn; ++e)
                         ((__bf16 *)dst)[e] = v[e];
@@ -1373,7 +1376,7 @@ __device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const typena
             } else {
                 const f32x4 v = v32;
                 if (t.vec_ok && c + 3 < t.vn) {
-                    *(f32x4 *)dst = v;
+                    __builtin_nontemporal_store(v, (f32x4 *)dst);
                 } else {
                     for (int e = 0; e < 4 && c + e < t.vn; ++e)
                         ((float *)dst)[e] = v[e];
