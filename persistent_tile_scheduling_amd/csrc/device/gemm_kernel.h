@@ -250,20 +250,27 @@ __device__ __forceinline__ void raster_tile(int local, int tiles_m, int tiles_n,
 }
 
 // Where a tile's k loop starts. Each compute die (XCD) works on a compact
-// block of tiles whose A and B panels its L2 shares, so within a block every
-// tile walks k in the same order. Across blocks the start is rotated by
-// K_PHASE k-tiles per block, so the dies do not all request the same k-slice
-// of memory at once. Each tile still sums every k-tile exactly once, in an
-// order fixed by its position alone, so every schedule and worker count
-// computes the same bits. A block is K_PHASE_BLOCK consecutive positions:
-// what the static dealing gives one die per round with one workgroup on each
-// of the 256 compute units (32 per die).
+// block of tiles whose A and B panels its L2 shares: RASTER_ROWS tile rows by
+// a few tile columns. Within a block, the tiles of one tile row start at the
+// same k-tile, so they read each A k-slice together; successive rows start
+// K_PHASE_ROW k-tiles apart, so the tiles of one column meet each B k-slice
+// one after another, the first bringing it into L2 for the rest, and the
+// block's requests at any moment spread over more of the L2. Across blocks
+// the start is rotated by K_PHASE k-tiles per block, so the dies do not all
+// request the same k-slice of memory at once. Each tile still sums every
+// k-tile exactly once, in an order fixed by its position alone, so every
+// schedule and worker count computes the same bits. A block is K_PHASE_BLOCK
+// consecutive positions: what the static dealing gives one die per round with
+// one workgroup on each of the 256 compute units (32 per die). Where a
+// problem's tiles start at a multiple of 8, position % 8 is the tile's row
+// inside its raster group (elsewhere it is just another fixed offset).
 constexpr int K_PHASE = 8;
+constexpr int K_PHASE_ROW = 2;
 constexpr int K_PHASE_BLOCK = 32;
 
 __device__ __forceinline__ int k_phase(int pos, int nk)
 {
-    return nk > 0 ? ((pos / K_PHASE_BLOCK) % NUM_XCD) * K_PHASE % nk : 0;
+    return nk > 0 ? (((pos / K_PHASE_BLOCK) % NUM_XCD) * K_PHASE + (pos % RASTER_ROWS) * K_PHASE_ROW) % nk : 0;
 }
 
 // The plan's problem table is never written while a kernel runs: read it
@@ -1093,7 +1100,9 @@ struct Mainloop {
 #pragma unroll
         for (int i = 0; i < C::LOADS; ++i)
             gload_one(i, min(1, nk - 1), t);
-        if (is_tail(0, t.k) && nk == 1) {
+        // the loop's first k-tile is the partial last one whenever the tile's
+        // rotated k order starts there
+        if (is_tail(0, t.k)) {
             wait_lgkmcnt0();
             zero_k_tail(0, 0, t.k);
         }
@@ -1183,7 +1192,9 @@ struct Mainloop {
             issue_any(s, s, t.k, nk);
         // k-tile 0: its loads were the oldest of the prologue
         wait_stage_loads<C, C::STAGES - 1>(min(C::STAGES - 1, nk - 1));
-        if (nk == 1 && is_tail(0, t.k))
+        // the loop's first k-tile is the partial last one whenever the tile's
+        // rotated k order starts there
+        if (is_tail(0, t.k))
             zero_k_tail(0, 0, t.k);
         barrier_lds();
         if (nk == 1)
