@@ -901,7 +901,7 @@ struct Mainloop {
     static constexpr int S_MFMAS = C::MI * C::NI;
     static constexpr int S_READS = C::MI + C::NI;
     static constexpr int READ_EVERY = 3; // one read after every third MFMA
-    static constexpr int LOAD_EVERY = 2; // one load after every second MFMA
+    static constexpr int LOAD_EVERY = 3; // one load after every third MFMA (16 loads over 48 of 64)
 
     // Fragment read r of a k-step, in the order the next k-step first needs
     // them: A0, B0 .. B(NI-1), A1 .. A(MI-1).
