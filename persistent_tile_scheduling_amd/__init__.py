@@ -35,6 +35,7 @@ GEMM_SCHEDULE_DYNAMIC_XCD = 2
 GEMM_SCHEDULE_NONPERSISTENT = 3
 GEMM_SCHED_COUNTER_BYTES = 36864
 GEMM_MAX_GROUPS = 64
+GEMM_TILE_AUTO = -1
 GEMM_FLAG_NONE = 0
 GEMM_FLAG_STAGE_FLAGS_FUSED = 1
 GEMM_FLAG_STAGE_FLAGS_MERGED = 2
@@ -140,7 +141,12 @@ def make_desc(shapes, dtype_d: int = GEMM_DTYPE_F32, tile=(0, 0, 0, 0, 0, 0, 0),
                                                                            GEMM_ROW_MAJOR),
               dtypes=(GEMM_DTYPE_BF16, GEMM_DTYPE_BF16, GEMM_DTYPE_F32)):
     """Build a ``gemm_desc``. ``shapes`` is a list of (m, n, k[, lda, ldb, ldd]);
-    ``tile`` is (tile_m, tile_n[, tile_k, stages, load_path, waves, mfma]) with 0 for defaults."""
+    ``tile`` is (tile_m, tile_n[, tile_k, stages, load_path, waves, mfma]) with 0 for defaults,
+    or "auto" for tile_m = tile_n = GEMM_TILE_AUTO (chosen by size)."""
+    if isinstance(tile, str):
+        if tile != "auto":
+            raise ValueError(f"tile must be a tuple or 'auto', not {tile!r}")
+        tile = (GEMM_TILE_AUTO, GEMM_TILE_AUTO)
     arr = (GemmShape * max(1, len(shapes)))()
     for i, s in enumerate(shapes):
         s = tuple(s) + (0,) * (6 - len(s))
@@ -218,7 +224,8 @@ def pts_sched_probe(num_tiles: int, num_workers: int, schedule: int, gate_worker
 
 class Plan:
     """Owns one ``gemm_plan``. ``shapes``: list of (m, n, k[, lda, ldb, ldd]);
-    ``tile``: (tile_m, tile_n[, tile_k, stages, load_path, waves]), 0 = default."""
+    ``tile``: (tile_m, tile_n[, tile_k, stages, load_path, waves, mfma]), 0 = default,
+    or "auto" (the library picks the tile edge from the sizes)."""
 
     def __init__(self, shapes, out_dtype=torch.float32, tile=(0, 0), schedule: str | int = "static",
                  num_workers: int = 0, flags: int = GEMM_FLAG_NONE):
@@ -279,11 +286,12 @@ def decode_trace(buf: torch.Tensor, num_tiles: int, num_workers: int):
     return tiles, workers
 
 
-def gemm(a: torch.Tensor, b: torch.Tensor, out_dtype=torch.float32, schedule="static", tile=(0, 0),
+def gemm(a: torch.Tensor, b: torch.Tensor, out_dtype=torch.float32, schedule="static", tile="auto",
          num_workers: int = 0, out: torch.Tensor | None = None, k: int | None = None) -> torch.Tensor:
     """D = A . B for A (m x lda, row-major) and B given as (n x ldb) = B^T row-major.
 
-    ``k`` defaults to ``a.shape[1]`` (no padding). Builds a one-shot plan.
+    ``k`` defaults to ``a.shape[1]`` (no padding). Builds a one-shot plan; the tile
+    defaults to the library's choice for the sizes ("auto").
     """
     m, lda = a.shape
     n, ldb = b.shape

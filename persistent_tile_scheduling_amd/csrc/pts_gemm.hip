@@ -129,6 +129,26 @@ const char *gemm_status_string(gemm_status s)
 
 const char *gemm_last_error(void) { return g_last_error.c_str(); }
 
+// Tile edge for GEMM_TILE_AUTO: the largest of 256, 128 and 64 whose tile
+// count (over all problems) fills at least half the compute units. Large
+// tiles read the least memory per flop, but a problem with fewer tiles than
+// half the chip leaves most of it idle for the whole run; from measurement
+// on 1024^3 .. 6144^3 bf16, this rule picks the fastest of the three edges.
+static int auto_tile_edge(const gemm_desc *desc, int cus)
+{
+    for (int edge : {256, 128}) {
+        int64_t tiles = 0;
+        for (int g = 0; g < desc->group_count; ++g) {
+            const gemm_shape &s = desc->shapes[g];
+            if (s.m > 0 && s.n > 0)
+                tiles += ((s.m + edge - 1) / edge) * ((s.n + edge - 1) / edge);
+        }
+        if (2 * tiles >= cus)
+            return edge;
+    }
+    return 64;
+}
+
 gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
 {
     if (out_plan == nullptr)
@@ -169,8 +189,22 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
                                                                       : pts::SYNC_BARRIER;
     if ((desc->flags & GEMM_FLAG_DEBUG_STAGE_FLAG_STALL) != 0 && sync == pts::SYNC_BARRIER)
         return fail(GEMM_ERR_INVALID_VALUE, "the stall test flag needs a stage-flag layout");
+    const bool auto_tile = desc->tile_m == GEMM_TILE_AUTO || desc->tile_n == GEMM_TILE_AUTO;
+    if (auto_tile && (desc->tile_m != desc->tile_n || desc->tile_k != 0 || desc->stages != 0 ||
+                      desc->load_path != 0 || desc->waves != 0 || desc->mfma != 0 || sync != pts::SYNC_BARRIER))
+        return fail(GEMM_ERR_INVALID_VALUE,
+                    "an automatic tile takes no other kernel choice (tile_m = tile_n = GEMM_TILE_AUTO, the rest 0)");
     int tm = desc->tile_m == 0 ? 256 : desc->tile_m;
     int tn = desc->tile_n == 0 ? 256 : desc->tile_n;
+    if (auto_tile) {
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess)
+            return hip_fail(e, "querying the compute unit count");
+        tm = tn = auto_tile_edge(desc, cus);
+    }
     const bool out_bf16 = desc->dtype_d == GEMM_DTYPE_BF16;
     const KernelEntry *entry = nullptr;
     if (desc->tile_k < 0 || desc->stages < 0 || desc->load_path < 0 || desc->load_path > 2 ||

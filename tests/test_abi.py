@@ -63,6 +63,10 @@ def test_status_strings(binding):
     (dict(flags=1, tile=(256, 256, 0, 0, 0, 8, 32)), 2, "stage flags"),
     (dict(flags=8), 1, "stall test flag"),
     (dict(tile=(96, 96)), 2, "not built"),
+    (dict(tile=(-1, 256)), 1, "automatic tile"),
+    (dict(tile=(-1, -1, 64)), 1, "automatic tile"),
+    (dict(tile=(-1, -1, 0, 0, 0, 8)), 1, "automatic tile"),
+    (dict(tile="auto", flags=1), 1, "automatic tile"),
 ])
 def test_plan_create_rejects_bad_descriptors(binding, kwargs, status, fragment):
     with pytest.raises(binding.GemmError) as ei:
@@ -129,6 +133,10 @@ def test_header_constants_match_the_binding(binding):
     defines = dict(re.findall(r"#define (GEMM_[A-Z_]+) (\d+)", text))
     assert defines, "no numeric constants found in the header"
     for name, value in defines.items():
+        assert getattr(binding, name) == int(value), name
+    negative = dict(re.findall(r"#define (GEMM_[A-Z_]+) \((-\d+)\)", text))
+    assert "GEMM_TILE_AUTO" in negative
+    for name, value in negative.items():
         assert getattr(binding, name) == int(value), name
     enums = dict(re.findall(r"(GEMM_SCHEDULE_[A-Z_]+) = (\d+)", text))
     for name, value in enums.items():
