@@ -29,7 +29,11 @@
  *   B: K x N, column-major, B[k][j] = b[j * ldb + k], bf16
  *   D: M x N, row-major,    D[i][j] = d[i * ldd + j], fp32 or bf16
  * Products are exact and accumulate in fp32 (MFMA). bf16 output rounds the
- * fp32 sum to nearest, ties to even.
+ * fp32 sum to nearest, ties to even. A tile sums its k-tiles in a rotated
+ * order that starts at a k-tile fixed by the tile's position in the plan (so
+ * that the compute dies do not all read the same k-slice at once): results
+ * are deterministic, equal across schedules and worker counts, and differ
+ * from a left-to-right fp32 sum only by rounding order.
  *
  * Memory: every pointer is device memory owned by the caller; the library
  * never allocates, frees or reads host copies of operand data. A plan owns a
