@@ -80,6 +80,8 @@ struct GemmArgs {
     int32_t schedule;
     int32_t round;     // static dealing width (see static_position)
     int32_t full_excess; // test only: added to every stage-flag full target (0 in normal runs)
+    int32_t k_phase_row; // k-tiles between successive tile rows' k starts (see k_phase)
+    int32_t pad0;
     uint64_t d_vec_ok; // bit g: problem g's D rows allow vector stores
     const uint16_t *a[PTS_MAX_GROUPS];
     const uint16_t *b[PTS_MAX_GROUPS];
@@ -253,24 +255,26 @@ __device__ __forceinline__ void raster_tile(int local, int tiles_m, int tiles_n,
 // block of tiles whose A and B panels its L2 shares: RASTER_ROWS tile rows by
 // a few tile columns. Within a block, the tiles of one tile row start at the
 // same k-tile, so they read each A k-slice together; successive rows start
-// K_PHASE_ROW k-tiles apart, so the tiles of one column meet each B k-slice
+// `row_step` k-tiles apart, so the tiles of one column meet each B k-slice
 // one after another, the first bringing it into L2 for the rest, and the
-// block's requests at any moment spread over more of the L2. Across blocks
-// the start is rotated by K_PHASE k-tiles per block, so the dies do not all
+// block's requests at any moment spread over more of the L2. (The plan sets
+// row_step to 0 for runs of many rounds, where the workers of a die drift
+// apart and the extra offset only breaks the sharing.) Across blocks the
+// start is rotated by K_PHASE k-tiles per block, so the dies do not all
 // request the same k-slice of memory at once. Each tile still sums every
-// k-tile exactly once, in an order fixed by its position alone, so every
-// schedule and worker count computes the same bits. A block is K_PHASE_BLOCK
-// consecutive positions: what the static dealing gives one die per round with
-// one workgroup on each of the 256 compute units (32 per die). Where a
-// problem's tiles start at a multiple of 8, position % 8 is the tile's row
-// inside its raster group (elsewhere it is just another fixed offset).
+// k-tile exactly once, in an order fixed by its position and the problem set
+// alone, so every schedule and worker count computes the same bits. A block
+// is K_PHASE_BLOCK consecutive positions: what the static dealing gives one
+// die per round with one workgroup on each of the 256 compute units (32 per
+// die). Where a problem's tiles start at a multiple of 8, position % 8 is the
+// tile's row inside its raster group (elsewhere it is just another fixed
+// offset).
 constexpr int K_PHASE = 8;
-constexpr int K_PHASE_ROW = 2;
 constexpr int K_PHASE_BLOCK = 32;
 
-__device__ __forceinline__ int k_phase(int pos, int nk)
+__device__ __forceinline__ int k_phase(int pos, int nk, int row_step)
 {
-    return nk > 0 ? (((pos / K_PHASE_BLOCK) % NUM_XCD) * K_PHASE + (pos % RASTER_ROWS) * K_PHASE_ROW) % nk : 0;
+    return nk > 0 ? (((pos / K_PHASE_BLOCK) % NUM_XCD) * K_PHASE + (pos % RASTER_ROWS) * row_step) % nk : 0;
 }
 
 // The plan's problem table is never written while a kernel runs: read it
@@ -314,7 +318,7 @@ __device__ __forceinline__ TileCtx<C> decode_tile(KernArgs args, int t, int grou
     c.vn = min(C::BN, gd.n - c.col0);
     c.k = gd.k;
     c.nk = gd.num_k_tiles;
-    c.kt0 = k_phase(t, c.nk);
+    c.kt0 = k_phase(t, c.nk, args->k_phase_row);
     c.lda = gd.lda;
     c.ldb = gd.ldb;
     c.ldd = gd.ldd;

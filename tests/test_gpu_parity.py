@@ -116,19 +116,24 @@ def test_k_tail_first_in_rotated_order(pts, tile):
     """256 tile positions and an odd number of k-tiles: the tiles' rotated k
     orders then start at every k-tile, the partial last one included, which is
     then the first k-tile the loop loads (its k >= K part must be zeroed before
-    the first fragment reads). Every tile is checked at its four corners."""
+    the first fragment reads). For 256x256 tiles also 1156 positions (more than
+    four rounds of the chip, where tile rows share their k start): some k
+    orders start at the partial k-tile there too. Every tile is checked at its
+    four corners."""
     bm = tile[0]
-    m = n = 16 * bm
     k = 520  # 9 k-tiles of 64 or 17 of 32; the last holds 8 values of k
     seed = 23
-    a = U.device_uniform(m, k, seed, 1)
-    b = U.device_uniform(n, k, seed, 2)
-    (rows, cols), = U.sample_entries([(m, n)], bm, bm, 300, seed=3)
-    ref = U.oracle_sampled(seed, 1, 2, k, rows, cols)
-    for sched in ("static", "dynamic_xcd"):
-        U.log(f"k tail first tile {tile} {sched} {m}x{n}x{k}")
-        d, _, _ = U.run_single(m, n, k, a, b, torch.float32, sched, tile=tile)
-        U.check_sampled(d, rows, cols, ref, k, f"k tail first tile {tile} {sched}")
+    for edge_tiles in ((16, 34) if bm == 256 else (16,)):
+        m = n = edge_tiles * bm
+        a = U.device_uniform(m, k, seed, 1)
+        b = U.device_uniform(n, k, seed, 2)
+        (rows, cols), = U.sample_entries([(m, n)], bm, bm, 300, seed=3)
+        ref = U.oracle_sampled(seed, 1, 2, k, rows, cols)
+        for sched in ("static", "dynamic_xcd"):
+            U.log(f"k tail first tile {tile} {sched} {m}x{n}x{k}")
+            d, _, _ = U.run_single(m, n, k, a, b, torch.float32, sched, tile=tile)
+            U.check_sampled(d, rows, cols, ref, k, f"k tail first tile {tile} {sched} {m}x{n}")
+        del a, b, d
 
 
 @pytest.mark.parametrize("tile", KERNELS)
