@@ -139,9 +139,9 @@ typedef struct {
 
 /*
  * tile_m = tile_n = GEMM_TILE_AUTO: gemm_plan_create picks the output tile
- * from the problem sizes and the device: the largest of 256x256, 128x128 and
- * 64x64 whose tile count (over all problems) fills at least half the compute
- * units, each with its default kernel. Large tiles read the least memory per
+ * from the problem sizes and the device: the first of 256x256, 256x128 and
+ * 128x128 whose tile count (over all problems) reaches 55% of the compute
+ * units, else 64x64, each with its default kernel. Large tiles read the least memory per
  * flop; a problem with too few of them leaves most of the chip idle. The other
  * kernel fields (tile_k, stages, load_path, waves, mfma) must then be 0 and no
  * stage-flag layout requested, else GEMM_ERR_INVALID_VALUE. This needs a
@@ -161,7 +161,7 @@ typedef struct {
     int32_t dtype_acc;         /* GEMM_DTYPE_F32 */
     int32_t dtype_d;           /* GEMM_DTYPE_F32 or GEMM_DTYPE_BF16 */
     int32_t tile_m, tile_n;    /* output tile; 0 = 256, GEMM_TILE_AUTO = chosen by size. Built: 256x256,
-                                  128x128, 64x64 */
+                                  256x128, 128x128, 64x64 */
     int32_t tile_k;            /* k-tile depth of one LDS ring stage: 0 = default, 32 or 64 */
     int32_t stages;            /* LDS ring stages: 0 = default for tile_k (64: 2, 32: 4) */
     int32_t load_path;         /* how a ring stage is filled: 0 = default, 1 = global->LDS loads,

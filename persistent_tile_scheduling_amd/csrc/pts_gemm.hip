@@ -78,6 +78,11 @@ const std::vector<KernelEntry> &kernel_table()
         make_entry<256, 256, 64, 2, false, pts::LOAD_DMA, 2, 2, 16>(),
         make_entry<256, 256, 32, 4, true>(),  make_entry<256, 256, 32, 4, false>(),
         make_entry<256, 256, 64, 2, true, pts::LOAD_REG>(), make_entry<256, 256, 64, 2, false, pts::LOAD_REG>(),
+        // 256x128: the default kernel's layout on half the columns (8 waves,
+        // 128x32 each), for problems whose 256x256 tile count leaves a
+        // partial last round
+        make_entry<256, 128, 64, 2, true, pts::LOAD_DMA, 2, 4, 16>(),
+        make_entry<256, 128, 64, 2, false, pts::LOAD_DMA, 2, 4, 16>(),
         make_entry<128, 128, 64, 2, true>(),  make_entry<128, 128, 64, 2, false>(),
         make_entry<128, 128, 32, 4, true>(),  make_entry<128, 128, 32, 4, false>(),
         make_entry<64, 64, 64, 2, true>(),    make_entry<64, 64, 64, 2, false>(),
@@ -130,24 +135,28 @@ const char *gemm_status_string(gemm_status s)
 
 const char *gemm_last_error(void) { return g_last_error.c_str(); }
 
-// Tile edge for GEMM_TILE_AUTO: the largest of 256, 128 and 64 whose tile
-// count (over all problems) fills at least half the compute units. Large
-// tiles read the least memory per flop, but a problem with fewer tiles than
-// half the chip leaves most of it idle for the whole run; from measurement
-// on 1024^3 .. 6144^3 bf16, this rule picks the fastest of the three edges.
-static int auto_tile_edge(const gemm_desc *desc, int cus)
+// Output tile for GEMM_TILE_AUTO: the first of 256x256, 256x128, 128x128
+// whose tile count (over all problems) reaches 55% of the compute units, else
+// 64x64. Larger tiles read less memory per flop, but a problem with too few of
+// them leaves most of the chip idle for the whole run; on bf16 squares from
+// 1024^3 to 6144^3 this rule picks the fastest of the four tiles.
+static void pick_auto_tile(const gemm_desc *desc, int cus, int &tm, int &tn)
 {
-    for (int edge : {256, 128}) {
+    static const int cand[3][2] = {{256, 256}, {256, 128}, {128, 128}};
+    for (const auto &c : cand) {
         int64_t tiles = 0;
         for (int g = 0; g < desc->group_count; ++g) {
             const gemm_shape &s = desc->shapes[g];
             if (s.m > 0 && s.n > 0)
-                tiles += ((s.m + edge - 1) / edge) * ((s.n + edge - 1) / edge);
+                tiles += ((s.m + c[0] - 1) / c[0]) * ((s.n + c[1] - 1) / c[1]);
         }
-        if (2 * tiles >= cus)
-            return edge;
+        if (20 * tiles >= 11 * (int64_t)cus) {
+            tm = c[0];
+            tn = c[1];
+            return;
+        }
     }
-    return 64;
+    tm = tn = 64;
 }
 
 gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
@@ -204,7 +213,7 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
             e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess)
             return hip_fail(e, "querying the compute unit count");
-        tm = tn = auto_tile_edge(desc, cus);
+        pick_auto_tile(desc, cus, tm, tn);
     }
     const bool out_bf16 = desc->dtype_d == GEMM_DTYPE_BF16;
     const KernelEntry *entry = nullptr;

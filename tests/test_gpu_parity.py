@@ -77,7 +77,8 @@ SWEEP = [(1, 1, 1), (7, 7, 7), (63, 65, 64), (64, 64, 64), (65, 63, 65), (127, 1
 # every built kernel: (tile_m, tile_n, tile_k, stages, load path, waves[, mfma])
 KERNELS = [(64, 64, 64, 2, 1, 4), (128, 128, 64, 2, 1, 4), (128, 128, 32, 4, 1, 4), (256, 256, 64, 2, 1, 4),
            (256, 256, 32, 4, 1, 4), (256, 256, 64, 2, 2, 4), (256, 256, 64, 2, 2, 8), (256, 256, 64, 2, 1, 8, 32),
-           (256, 256, 32, 4, 1, 8), (256, 256, 64, 2, 1, 8, 16), (256, 256, 64, 2, 1, 4, 16)]
+           (256, 256, 32, 4, 1, 8), (256, 256, 64, 2, 1, 8, 16), (256, 256, 64, 2, 1, 4, 16),
+           (256, 128, 64, 2, 1, 8, 16)]
 
 
 @pytest.mark.parametrize("tile", KERNELS)
@@ -157,7 +158,8 @@ def test_rotated_k_order_with_k_tail(pts, tile):
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("tile", [(256, 256, 64, 2, 1, 4), (256, 256, 32, 4, 1, 4), (256, 256, 64, 2, 2, 4),
                                   (256, 256, 64, 2, 2, 8), (256, 256, 64, 2, 1, 8, 32), (256, 256, 32, 4, 1, 8),
-                                  (256, 256, 64, 2, 1, 8, 16), (256, 256, 64, 2, 1, 4, 16)])
+                                  (256, 256, 64, 2, 1, 8, 16), (256, 256, 64, 2, 1, 4, 16),
+                                  (256, 128, 64, 2, 1, 8, 16)])
 def test_random_ragged_full_oracle(pts, shape, out_dtype, tile):
     m, n, k = shape
     lda, ldb, ldd = _padded_ld(k) + 16, _padded_ld(k) + 8, n + 5
