@@ -145,8 +145,8 @@ typedef struct {
  * flop; a problem with too few of them leaves most of the chip idle. The other
  * kernel fields (tile_k, stages, load_path, waves, mfma) must then be 0 and no
  * stage-flag layout requested, else GEMM_ERR_INVALID_VALUE. This needs a
- * current HIP device (GEMM_ERR_HIP otherwise); gemm_plan_query reports nothing
- * of the choice except through num_tiles.
+ * current HIP device (GEMM_ERR_HIP otherwise); gemm_plan_query_kernel reports
+ * the tile chosen.
  */
 #define GEMM_TILE_AUTO (-1)
 
@@ -228,6 +228,13 @@ gemm_status gemm_plan_destroy(gemm_plan *plan);
  * Any output pointer may be NULL. */
 gemm_status gemm_plan_query(const gemm_plan *plan, int64_t *num_tiles, int32_t *num_workers,
                             int32_t *lds_bytes);
+
+/* The kernel a plan runs: output tile (tile_m x tile_n, also when the
+ * descriptor asked for GEMM_TILE_AUTO), k-tile depth, ring stages, waves per
+ * workgroup and MFMA block edge (16 or 32). Any output pointer may be NULL;
+ * GEMM_ERR_INVALID_VALUE for a NULL plan. */
+gemm_status gemm_plan_query_kernel(const gemm_plan *plan, int32_t *tile_m, int32_t *tile_n, int32_t *tile_k,
+                                   int32_t *stages, int32_t *waves, int32_t *mfma);
 
 /*
  * Per-tile trace (test and benchmark use). After this call every run writes,

@@ -85,6 +85,7 @@ def _load():
         "gemm_plan_destroy": (ctypes.c_int, [P]),
         "gemm_plan_query": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32),
                                            ctypes.POINTER(ctypes.c_int32)]),
+        "gemm_plan_query_kernel": (ctypes.c_int, [P] + [ctypes.POINTER(ctypes.c_int32)] * 6),
         "gemm_plan_set_trace": (ctypes.c_int, [P, P, ctypes.c_size_t]),
         "gemm_plan_read_counters": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_uint32)]),
         "pts_copy_int16": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32, P]),
@@ -183,6 +184,13 @@ def gemm_plan_query(plan: int) -> tuple[int, int, int]:
     return t.value, w.value, l.value
 
 
+def gemm_plan_query_kernel(plan: int) -> dict:
+    """The plan's kernel: tile_m, tile_n, tile_k, stages, waves, mfma."""
+    vals = [ctypes.c_int32() for _ in range(6)]
+    _check(_lib.gemm_plan_query_kernel(ctypes.c_void_p(plan), *[ctypes.byref(v) for v in vals]))
+    return dict(zip(("tile_m", "tile_n", "tile_k", "stages", "waves", "mfma"), (v.value for v in vals)))
+
+
 def gemm_plan_set_trace(plan: int, device_buf, nbytes: int) -> None:
     _check(_lib.gemm_plan_set_trace(ctypes.c_void_p(plan), ctypes.c_void_p(_ptr(device_buf)), nbytes))
 
@@ -240,6 +248,7 @@ class Plan:
         self.desc = make_desc(self.shapes, dtype_d, tile, schedule, num_workers, flags)
         self.handle = gemm_plan_create(self.desc)
         self.num_tiles, self.num_workers, self.lds_bytes = gemm_plan_query(self.handle)
+        self.kernel = gemm_plan_query_kernel(self.handle)
 
     def run(self, operands, stream=None) -> None:
         gemm_run(self.handle, operands, stream)

@@ -408,6 +408,20 @@ gemm_status gemm_plan_query(const gemm_plan *plan, int64_t *num_tiles, int32_t *
     return GEMM_OK;
 }
 
+gemm_status gemm_plan_query_kernel(const gemm_plan *plan, int32_t *tile_m, int32_t *tile_n, int32_t *tile_k,
+                                   int32_t *stages, int32_t *waves, int32_t *mfma)
+{
+    if (plan == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "plan is NULL");
+    if (tile_m) *tile_m = plan->kernel.bm;
+    if (tile_n) *tile_n = plan->kernel.bn;
+    if (tile_k) *tile_k = plan->kernel.bk;
+    if (stages) *stages = plan->kernel.stages;
+    if (waves) *waves = plan->kernel.waves;
+    if (mfma) *mfma = plan->kernel.mfma;
+    return GEMM_OK;
+}
+
 gemm_status gemm_plan_set_trace(gemm_plan *plan, void *device_buf, size_t bytes)
 {
     if (plan == nullptr)

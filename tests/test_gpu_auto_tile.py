@@ -53,6 +53,7 @@ def test_auto_tile_choice_and_parity(pts, shapes, out_dtype):
         samples.append((rows, cols, U.oracle_sampled(40 + i, 1, 2, k, rows, cols)))
     with pts.Plan(shapes, out_dtype, "auto", "dynamic_xcd") as p:
         assert p.num_tiles == _tiles(shapes, tm, tn)
+        assert (p.kernel["tile_m"], p.kernel["tile_n"]) == (tm, tn)
         p.run(ops)
         torch.cuda.synchronize()
         U.check_counters("dynamic_xcd", p.counters(), p.num_tiles, p.num_workers)
