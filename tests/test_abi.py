@@ -154,3 +154,10 @@ def test_plan_create_rejects_sizes_beyond_the_limits(binding, shape, fragment):
         binding.gemm_plan_create(binding.make_desc([shape]))
     assert ei.value.status in (binding.GEMM_ERR_INVALID_VALUE, binding.GEMM_ERR_UNSUPPORTED)
     assert fragment in str(ei.value)
+
+
+def test_tile_strings_other_than_auto_are_rejected(binding):
+    with pytest.raises(ValueError):
+        binding.make_desc([(64, 64, 64)], tile="largest")
+    d = binding.make_desc([(64, 64, 64)], tile="auto")
+    assert (d.tile_m, d.tile_n) == (binding.GEMM_TILE_AUTO, binding.GEMM_TILE_AUTO)
