@@ -64,6 +64,7 @@ class OracleLib:
         lib.oracle_gemm.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                     _u16p, ctypes.c_int64, _u16p, ctypes.c_int64,
                                     _f64p, ctypes.c_int64, ctypes.c_int]
+        lib.oracle_gemm.restype = ctypes.c_int
         lib.oracle_gemm_entries.argtypes = [ctypes.c_int64, _u16p, ctypes.c_int64,
                                             _u16p, ctypes.c_int64, ctypes.c_int64,
                                             _i64p, _i64p, _f64p, ctypes.c_int]
@@ -99,10 +100,12 @@ class OracleLib:
         a = _u16(a_bits).reshape(-1)
         b = _u16(b_bits).reshape(-1)
         _check_operands(m, n, k, a, lda, b, ldb)
-        d = np.zeros((m, n), dtype=np.float64)
+        # NaN-filled: an element the C loop failed to clear or write shows up
+        d = np.full((m, n), np.nan, dtype=np.float64)
         if m and n:
-            self.lib.oracle_gemm(m, n, k, a.ctypes.data_as(_u16p), lda, b.ctypes.data_as(_u16p), ldb,
-                                 d.ctypes.data_as(_f64p), n, threads)
+            if self.lib.oracle_gemm(m, n, k, a.ctypes.data_as(_u16p), lda, b.ctypes.data_as(_u16p), ldb,
+                                    d.ctypes.data_as(_f64p), n, threads) != 0:
+                raise MemoryError(f"oracle: no memory for the row-major copy of B ({k} x {n})")
         return d
 
     def gemm_entries(self, a_bits, b_bits, k: int, rows, cols, lda: int | None = None,

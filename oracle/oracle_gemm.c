@@ -31,16 +31,18 @@
  * the IEEE-754 definition (scale to the target grid, round, scale back); the
  * pages do not name a rounding, and this is the IEEE default.
  *
- * Parallelism: OpenMP over output rows only. Every element's summation order
- * is fixed, so the result does not depend on the thread count.
+ * Parallelism: OpenMP over output rows only (and over k for the copy of B).
+ * Every element's summation order is fixed, so the result does not depend on
+ * the thread count.
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #include <omp.h>
 
 /* bf16 bits -> double, exact. */
-double oracle_bf16_decode(uint16_t bits)
+static inline double decode(uint16_t bits)
 {
     uint32_t u = (uint32_t)bits << 16;
     float f;
@@ -48,10 +50,12 @@ double oracle_bf16_decode(uint16_t bits)
     return (double)f;
 }
 
+double oracle_bf16_decode(uint16_t bits) { return decode(bits); }
+
 void oracle_bf16_decode_array(const uint16_t *bits, double *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i)
-        out[i] = oracle_bf16_decode(bits[i]);
+        out[i] = decode(bits[i]);
 }
 
 /*
@@ -107,22 +111,44 @@ int oracle_max_threads(void)
 /*
  * Full product: D (m x n, row-major, ldd) = A (m x k, row-major, lda)
  *                                          * B (k x n, column-major, ldb).
+ *
+ * Loop order i, k, j: for one output row i, every element D[i][j] holds its
+ * own double accumulator, which starts at zero and receives the products
+ * A[i][k] * B[k][j] for k = 0, 1, ..., K-1 in that order -- the same additions,
+ * in the same order, with the same roundings as a per-element k loop. Only
+ * which element is advanced next changes, so the result is bit-identical to
+ * the i, j, k triple loop (oracle_gemm_entries computes single elements that
+ * way). With j innermost, B is read along its rows, so a copy of B with its
+ * rows contiguous (bt[kk * n + j] = B[kk][j], the bf16 bit patterns moved, not
+ * changed) is made first. Returns 0, or -1 if that copy cannot be allocated.
  */
-void oracle_gemm(int64_t m, int64_t n, int64_t k,
-                 const uint16_t *a, int64_t lda,
-                 const uint16_t *b, int64_t ldb,
-                 double *d, int64_t ldd, int nthreads)
+int oracle_gemm(int64_t m, int64_t n, int64_t k,
+                const uint16_t *a, int64_t lda,
+                const uint16_t *b, int64_t ldb,
+                double *d, int64_t ldd, int nthreads)
 {
     set_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
+    uint16_t *bt = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(k * n > 0 ? k * n : 1));
+    if (bt == NULL)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t kk = 0; kk < k; ++kk)
+        for (int64_t j = 0; j < n; ++j)
+            bt[kk * n + j] = b[j * ldb + kk];
+#pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < m; ++i) {
-        for (int64_t j = 0; j < n; ++j) {
-            double acc = 0.0;
-            for (int64_t kk = 0; kk < k; ++kk)
-                acc += oracle_bf16_decode(a[i * lda + kk]) * oracle_bf16_decode(b[j * ldb + kk]);
-            d[i * ldd + j] = acc;
+        double *drow = d + i * ldd;
+        for (int64_t j = 0; j < n; ++j)
+            drow[j] = 0.0;
+        for (int64_t kk = 0; kk < k; ++kk) {
+            const double aik = decode(a[i * lda + kk]);
+            const uint16_t *brow = bt + kk * n;
+            for (int64_t j = 0; j < n; ++j)
+                drow[j] += aik * decode(brow[j]);
         }
     }
+    free(bt);
+    return 0;
 }
 
 /*
@@ -141,7 +167,7 @@ void oracle_gemm_entries(int64_t k,
         const int64_t i = rows[e], j = cols[e];
         double acc = 0.0;
         for (int64_t kk = 0; kk < k; ++kk)
-            acc += oracle_bf16_decode(a[i * lda + kk]) * oracle_bf16_decode(b[j * ldb + kk]);
+            acc += decode(a[i * lda + kk]) * decode(b[j * ldb + kk]);
         out[e] = acc;
     }
 }

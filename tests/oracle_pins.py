@@ -22,6 +22,11 @@ What pins what:
 * ``pin_numpy_matmul`` -- on random inputs the result agrees with numpy's
   float64 matmul of the decoded matrices (an independent library routine)
   within a few float64 rounding errors of sum |a||b|.
+* ``pin_k_order`` -- products 1, 2^100, -2^100 (exact in bf16 and double):
+  summed k ascending they give (1 + 2^100) - 2^100 = 0, summed in any order
+  that adds the two large ones first they give 1: pins the summation order.
+* ``pin_entries_integer`` -- the per-entry form on integer-valued inputs
+  equals the same Python big-integer sums at every listed entry.
 * ``pin_decode_vs_torch`` -- bf16 decoding agrees with torch's bf16 -> float64
   conversion on all 65536 patterns.
 """
@@ -130,11 +135,35 @@ def pin_numpy_matmul(gemm, decode, m=67, n=45, k=301, seed=11):
         raise AssertionError("disagrees with numpy float64 matmul")
 
 
+def pin_k_order(gemm):
+    big = 0x7180        # 2^100 in bf16
+    a = np.array([[BF16_ONE, big, big | 0x8000]], dtype=np.uint16)   # 1, 2^100, -2^100
+    b = np.full((2, 3), BF16_ONE, dtype=np.uint16)
+    d = gemm(a, b, 1, 2, 3)
+    if not np.all(d == 0.0):
+        raise AssertionError(f"k order: got {d}, the ascending sum is 0")
+
+
+def pin_entries_integer(gemm_entries, seed=13):
+    for (m, n, k) in ((5, 4, 9), (3, 7, 1), (6, 6, 33)):
+        a = gen.operand_a(m, k, seed, kind="integer")
+        b = gen.operand_b(k, n, seed, kind="integer")
+        ia = _int_stream(seed, gen.TENSOR_A, m * k)
+        ib = _int_stream(seed, gen.TENSOR_B, n * k)
+        rows = np.repeat(np.arange(m), n)
+        cols = np.tile(np.arange(n), m)
+        got = gemm_entries(a, b, k, rows, cols)
+        for e, (i, j) in enumerate(zip(rows, cols)):
+            want = sum(ia[i * k + kk] * ib[j * k + kk] for kk in range(k))
+            if got[e] != want:
+                raise AssertionError(f"entries: shape {(m, n, k)} at {(i, j)}: {got[e]} != {want}")
+
+
 ALL_GEMM_PINS = ("integer_square", "integer", "identity", "permutation", "probes", "zero", "ones",
-                 "ties", "numpy")
+                 "ties", "numpy", "k_order", "entries_integer")
 
 
-def run_gemm_pins(gemm, decode, round_bf16, on_result=None):
+def run_gemm_pins(gemm, decode, round_bf16, on_result=None, gemm_entries=None):
     """Run every GEMM pin; return the names of those that failed.
 
     Square shapes run first: an index slip that swaps a dimension stays inside
@@ -151,7 +180,10 @@ def run_gemm_pins(gemm, decode, round_bf16, on_result=None):
         "ones": lambda: pin_ones(gemm),
         "ties": lambda: pin_bf16_ties(gemm, round_bf16, decode),
         "numpy": lambda: pin_numpy_matmul(gemm, decode),
+        "k_order": lambda: pin_k_order(gemm),
     }
+    if gemm_entries is not None:
+        checks["entries_integer"] = lambda: pin_entries_integer(gemm_entries)
     failed = []
     for name, fn in checks.items():
         try:

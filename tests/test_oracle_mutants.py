@@ -20,20 +20,34 @@ from oracle import build as obuild
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 MUTANTS = {
-    "drops_last_k": ("kk < k; ++kk)\n                acc +=", "kk < k - 1; ++kk)\n                acc +="),
-    "skips_first_k": ("for (int64_t kk = 0; kk < k; ++kk)\n                acc +=",
-                      "for (int64_t kk = 1; kk < k; ++kk)\n                acc +="),
-    "subtracts": ("acc += oracle_bf16_decode(a[i * lda + kk])", "acc -= oracle_bf16_decode(a[i * lda + kk])"),
-    "b_row_major": ("oracle_bf16_decode(b[j * ldb + kk]);\n            d[",
-                    "oracle_bf16_decode(b[kk * ldb + j]);\n            d["),
-    "a_uses_col": ("acc += oracle_bf16_decode(a[i * lda + kk]) * oracle_bf16_decode(b[j * ldb + kk]);\n            d[",
-                   "acc += oracle_bf16_decode(a[j * lda + kk]) * oracle_bf16_decode(b[j * ldb + kk]);\n            d["),
-    "d_transposed": ("d[i * ldd + j] = acc;", "d[j * ldd + i] = acc;"),
+    # the full product (i, k, j loop over the row-major copy of B)
+    "drops_last_k": ("for (int64_t kk = 0; kk < k; ++kk) {\n            const double aik",
+                     "for (int64_t kk = 0; kk < k - 1; ++kk) {\n            const double aik"),
+    "skips_first_k": ("for (int64_t kk = 0; kk < k; ++kk) {\n            const double aik",
+                      "for (int64_t kk = 1; kk < k; ++kk) {\n            const double aik"),
+    "subtracts": ("drow[j] += aik * decode(brow[j]);", "drow[j] -= aik * decode(brow[j]);"),
+    "b_row_major": ("bt[kk * n + j] = b[j * ldb + kk];", "bt[kk * n + j] = b[kk * ldb + j];"),
+    "a_uses_col": ("const double aik = decode(a[i * lda + kk]);", "const double aik = decode(a[kk * lda + i]);"),
+    "b_copy_transposed_twice": ("const uint16_t *brow = bt + kk * n;\n            for (int64_t j = 0; j < n; ++j)\n"
+                                "                drow[j] += aik * decode(brow[j]);",
+                                "const uint16_t *brow = bt + kk;\n            for (int64_t j = 0; j < n; ++j)\n"
+                                "                drow[j] += aik * decode(brow[j * k]);"),
+    "d_transposed": ("double *drow = d + i * ldd;", "double *drow = d + i;"),
+    "d_not_cleared": ("            drow[j] = 0.0;\n", "            drow[j] += 0.0;\n"),
     "decode_shift": ("(uint32_t)bits << 16", "(uint32_t)bits << 15"),
     "round_half_away": ("rint(ldexp(x, -q))", "round(ldexp(x, -q))"),
     "round_truncates": ("rint(ldexp(x, -q))", "trunc(ldexp(x, -q))"),
-    "accumulates_float": ("double acc = 0.0;\n            for (int64_t kk = 0; kk < k; ++kk)\n                acc +=",
-                          "float acc = 0.0f;\n            for (int64_t kk = 0; kk < k; ++kk)\n                acc += (float)"),
+    "accumulates_float": ("drow[j] += aik * decode(brow[j]);", "drow[j] = (float)(drow[j] + aik * decode(brow[j]));"),
+    # the per-entry form
+    "entries_drop_last_k": ("for (int64_t kk = 0; kk < k; ++kk)\n            acc +=",
+                            "for (int64_t kk = 0; kk < k - 1; ++kk)\n            acc +="),
+    "k_descending": ("for (int64_t kk = 0; kk < k; ++kk) {\n            const double aik = decode(a[i * lda + kk]);\n"
+                     "            const uint16_t *brow = bt + kk * n;",
+                     "for (int64_t k2 = 0; k2 < k; ++k2) {\n            const int64_t kk = k - 1 - k2;\n"
+                     "            const double aik = decode(a[i * lda + kk]);\n"
+                     "            const uint16_t *brow = bt + kk * n;"),
+    "entries_b_row_major": ("acc += decode(a[i * lda + kk]) * decode(b[j * ldb + kk]);",
+                            "acc += decode(a[i * lda + kk]) * decode(b[kk * ldb + j]);"),
 }
 
 _CHILD = r"""
@@ -44,7 +58,7 @@ from tests import oracle_pins as pins
 lib = oracle.OracleLib({lib!r})
 def report(name, ok):
     print(json.dumps([name, ok]), flush=True)
-pins.run_gemm_pins(lib.gemm, lib.bf16_decode, lib.bf16_round, on_result=report)
+pins.run_gemm_pins(lib.gemm, lib.bf16_decode, lib.bf16_round, on_result=report, gemm_entries=lib.gemm_entries)
 """
 
 

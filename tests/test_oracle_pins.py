@@ -13,7 +13,8 @@ from tests import oracle_pins as pins
 
 
 def test_gemm_pins_all_pass():
-    assert pins.run_gemm_pins(oracle.gemm, oracle.bf16_decode, oracle.bf16_round) == []
+    assert pins.run_gemm_pins(oracle.gemm, oracle.bf16_decode, oracle.bf16_round,
+                              gemm_entries=oracle.gemm_entries) == []
 
 
 def test_bf16_decode_exhaustive_vs_torch():
