@@ -162,14 +162,16 @@ typedef struct {
     int32_t dtype_d;           /* GEMM_DTYPE_F32 or GEMM_DTYPE_BF16 */
     int32_t tile_m, tile_n;    /* output tile; 0 = 256, GEMM_TILE_AUTO = chosen by size. Built: 256x256,
                                   256x128, 128x128, 64x64 */
-    int32_t tile_k;            /* k-tile depth of one LDS ring stage: 0 = default, 32 or 64 */
-    int32_t stages;            /* LDS ring stages: 0 = default for tile_k (64: 2, 32: 4) */
-    int32_t load_path;         /* how a ring stage is filled: 0 = default, 1 = global->LDS loads,
-                                  2 = global->registers->LDS (256x256, tile_k 64, 2 stages) */
-    int32_t waves;             /* waves per workgroup: 0 = default, 4 (one per SIMD) or 8 (two per
-                                  SIMD; 256x256 with tile_k 64 and 2 stages or tile_k 32 and 4) */
-    int32_t mfma;              /* matrix instruction: 0 = default, 32 (32x32x16) or 16 (16x16x32;
-                                  256x256, 8 waves, global->LDS loads) */
+    int32_t tile_k;            /* k-tile depth of one LDS ring stage: 0 or 64 (the only depth built) */
+    int32_t stages;            /* LDS ring stages: 0 or 2 (the only ring built) */
+    int32_t load_path;         /* how a ring stage is filled: 0 or 1 = global->LDS loads (the only path) */
+    int32_t waves;             /* waves per workgroup: 0 = default, 4 or 8. Built kernels:
+                                    256x256: 8 waves (two per SIMD) with 16x16x32 MFMAs (default), or
+                                             4 waves (one per SIMD) with 16x16x32 MFMAs;
+                                    256x128: 8 waves, 16x16x32;
+                                    128x128 and 64x64: 4 waves, 32x32x16 */
+    int32_t mfma;              /* matrix instruction: 0 = the tile's kernel, 16 (16x16x32) or 32 (32x32x16),
+                                  as listed above */
     int32_t schedule;          /* gemm_schedule */
     int32_t num_workers;       /* 0 = one per compute unit times occupancy, capped at the tile count */
     uint32_t flags;            /* GEMM_FLAG_* */
@@ -188,7 +190,11 @@ typedef struct {
     void *d;
 } gemm_operands;
 
-/* Message for a status code (static storage). */
+/* Message for a status code (static storage). The codes name the checks the
+ * pages ask for before anything runs: a mismatched configuration is rejected
+ * when it is put together, not at run time (CUTLASS Task Scheduling page
+ * "Pipeline Groups", section "How member configs are merged"; "Introduction",
+ * section "Authoring Lifecycle", step 6: validation before lowering). */
 const char *gemm_status_string(gemm_status status);
 
 /* Message describing the most recent failure on this thread ("" if none). */
@@ -207,7 +213,11 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan);
 
 /*
  * Run the plan: one persistent kernel launch on `stream` computing every
- * problem of the plan. `ops` is a host array of desc.group_count operand sets.
+ * problem of the plan. This is the pages' persistent schedule: a fixed grid of
+ * workers each running the work-tile loop, taking its next tile from the
+ * queue at the end of every iteration ("Schedules", sections "Persistent
+ * Scheduling" and "Scheduling Shapes"), the tile body being the GEMM
+ * mainloop of "Pipeline Groups", section "Overview". `ops` is a host array of desc.group_count operand sets.
  * Returns GEMM_ERR_INVALID_VALUE for a NULL or misaligned pointer (nothing is
  * launched), GEMM_ERR_HIP if the launch fails. Problems with m = 0 or n = 0
  * write nothing; k = 0 writes zeros. The run must be on the device the plan
@@ -219,13 +229,20 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan);
  */
 gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream);
 
-/* Free the plan and its device memory. NULL is a no-op. The caller must
- * ensure no run of the plan is still executing. */
+/* Free the plan and its device memory (the claim counters and the problem
+ * table, which the plan owns the way a pipeline group owns its shared barrier
+ * storage: "Pipeline Groups", section "Setup"). NULL is a no-op. The caller
+ * must ensure no run of the plan is still executing. GEMM_ERR_HIP if the
+ * runtime refuses the free (the plan's host part is released regardless). */
 gemm_status gemm_plan_destroy(gemm_plan *plan);
 
 /* Tile count, worker count (grid size; the tile count for the non-persistent
- * schedule) and LDS bytes per workgroup of a plan.
- * Any output pointer may be NULL. */
+ * schedule) and LDS bytes per workgroup of a plan: the size of the tile space
+ * the work queue hands out and of the persistent grid that drains it
+ * ("Schedules", section "Scheduling Shapes"; "Advanced scheduling: Cluster
+ * Launch Control", section "Limits of the static persistent scheduler", whose
+ * example has 12 tiles and 4 workers). Any output pointer may be NULL;
+ * GEMM_ERR_INVALID_VALUE for a NULL plan. */
 gemm_status gemm_plan_query(const gemm_plan *plan, int64_t *num_tiles, int32_t *num_workers,
                             int32_t *lds_bytes);
 
@@ -237,7 +254,11 @@ gemm_status gemm_plan_query_kernel(const gemm_plan *plan, int32_t *tile_m, int32
                                    int32_t *stages, int32_t *waves, int32_t *mfma);
 
 /*
- * Per-tile trace (test and benchmark use). After this call every run writes,
+ * Per-tile trace (test and benchmark use): which worker ran which tile, in
+ * what order and when -- the record behind the exactly-once and launch-tail
+ * statements of "Advanced scheduling: Cluster Launch Control", sections
+ * "Limits of the static persistent scheduler" and "One CLC request" (the
+ * 12-tile / 4-worker assignment table). After this call every run writes,
  * into `device_buf`, one record per tile followed by one record per worker:
  *
  *   struct { int32 tile, claim, worker, seq, group, row0, col0; uint32 xcc_id,
@@ -275,6 +296,20 @@ gemm_status gemm_plan_set_trace(gemm_plan *plan, void *device_buf, size_t bytes)
  * unless the stage hand-off is broken; see GEMM_FLAG_STAGE_FLAGS_FUSED).
  */
 gemm_status gemm_plan_read_counters(const gemm_plan *plan, uint32_t out[5]);
+
+/*
+ * Test only: set the dynamic schedules' claim counters (synchronizes the
+ * device), as if `value` claims had already been taken before the next run.
+ * GEMM_SCHEDULE_DYNAMIC: the single counter, so that run processes exactly
+ * the tiles value .. T-1 (value >= T: every worker's first claim fails and the
+ * run writes nothing). GEMM_SCHEDULE_DYNAMIC_XCD: every XCD's counter, so each
+ * XCD's sequence starts at its value-th entry. This replays the failed request
+ * of "Advanced scheduling: Cluster Launch Control", section "One CLC request"
+ * (a worker that finds the pool drained leaves its loop at once). The run's
+ * self-reset puts the counters back to 0 afterwards. GEMM_ERR_INVALID_VALUE for
+ * a NULL plan, another schedule, or value >= 2^24.
+ */
+gemm_status gemm_plan_preset_claims(gemm_plan *plan, uint32_t value);
 
 /*
  * Grid-stride int16 copy dst[i] = src[i] for 0 <= i < n, 16 bytes per lane per

@@ -88,6 +88,7 @@ def _load():
         "gemm_plan_query_kernel": (ctypes.c_int, [P] + [ctypes.POINTER(ctypes.c_int32)] * 6),
         "gemm_plan_set_trace": (ctypes.c_int, [P, P, ctypes.c_size_t]),
         "gemm_plan_read_counters": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_uint32)]),
+        "gemm_plan_preset_claims": (ctypes.c_int, [P, ctypes.c_uint32]),
         "pts_copy_int16": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32, P]),
         "pts_stream_create_cu_masked": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(P)]),
         "pts_stream_destroy": (ctypes.c_int, [P]),
@@ -201,6 +202,11 @@ def gemm_plan_read_counters(plan: int) -> list[int]:
     return list(out)
 
 
+def gemm_plan_preset_claims(plan: int, value: int) -> None:
+    """Test only: the dynamic schedules' claim counters start the next run at ``value``."""
+    _check(_lib.gemm_plan_preset_claims(ctypes.c_void_p(plan), value))
+
+
 def pts_copy_int16(src, dst, n: int, num_blocks: int = 0, stream=None) -> None:
     _check(_lib.pts_copy_int16(ctypes.c_void_p(_ptr(src)), ctypes.c_void_p(_ptr(dst)), n, num_blocks,
                                ctypes.c_void_p(_stream_handle(stream))))
@@ -256,6 +262,9 @@ class Plan:
     def counters(self) -> list[int]:
         return gemm_plan_read_counters(self.handle)
 
+    def preset_claims(self, value: int) -> None:
+        gemm_plan_preset_claims(self.handle, value)
+
     def trace_bytes(self) -> int:
         return TILE_TRACE_BYTES * self.num_tiles + WORKER_TRACE_BYTES * self.num_workers
 
@@ -297,16 +306,45 @@ def decode_trace(buf: torch.Tensor, num_tiles: int, num_workers: int):
 
 def gemm(a: torch.Tensor, b: torch.Tensor, out_dtype=torch.float32, schedule="static", tile="auto",
          num_workers: int = 0, out: torch.Tensor | None = None, k: int | None = None) -> torch.Tensor:
-    """D = A . B for A (m x lda, row-major) and B given as (n x ldb) = B^T row-major.
+    """D = A . B for a bf16 A (m x k, row-major) and B given as its transpose
+    (n x k, row-major: B's columns are the rows of ``b``).
 
-    ``k`` defaults to ``a.shape[1]`` (no padding). Builds a one-shot plan; the tile
+    ``a`` and ``b`` may be row slices or column slices of larger tensors
+    (``x[:, :k]``): their leading dimensions are taken from ``stride(0)``, which
+    must be a multiple of 8 elements, ``stride(1)`` must be 1 and the first
+    element 16-byte aligned. ``k``
+    defaults to ``a.shape[1]``. ``out`` (fp32 or bf16, m x n, ``stride(1) == 1``)
+    is written in place when given. Every tensor must be on the current GPU.
+    Anything else raises ``ValueError``. Builds a one-shot plan; the tile
     defaults to the library's choice for the sizes ("auto").
     """
-    m, lda = a.shape
-    n, ldb = b.shape
-    kk = lda if k is None else k
+    for name, t in (("a", a), ("b", b)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D bfloat16 tensor")
+    m, ka = a.shape
+    n, kb = b.shape
+    kk = ka if k is None else int(k)
+    if kk < 0 or kk > ka or kk > kb:
+        raise ValueError(f"k = {kk} exceeds the operands' widths ({ka}, {kb})")
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=a.device)
-    with Plan([(m, n, kk, lda, ldb, out.stride(0))], out.dtype, tile, schedule, num_workers) as p:
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.dim() != 2 or tuple(out.shape) != (m, n):
+        raise ValueError(f"out must be a 2-D fp32 or bf16 tensor of shape ({m}, {n})")
+    dev = torch.device("cuda", torch.cuda.current_device())
+    for name, t in (("a", a), ("b", b), ("out", out)):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, not on the current device {dev}")
+        if t.numel() and t.shape[1] > 1 and t.stride(1) != 1:
+            raise ValueError(f"{name} must have unit stride along its rows (stride(1) == 1)")
+    lda = a.stride(0) if m > 1 else 8 * ((kk + 7) // 8)
+    ldb = b.stride(0) if n > 1 else 8 * ((kk + 7) // 8)
+    ldd = out.stride(0) if m > 1 else n
+    if lda % 8 or ldb % 8:
+        raise ValueError(f"row strides of a and b ({lda}, {ldb}) must be multiples of 8 elements")
+    if kk and (a.data_ptr() % 16 or b.data_ptr() % 16):
+        raise ValueError("a and b must start 16-byte aligned (a column slice must start at a multiple of 8)")
+    if ldd < n:
+        raise ValueError(f"out's row stride {ldd} is below n = {n}")
+    with Plan([(m, n, kk, lda, ldb, ldd)], out.dtype, tile, schedule, num_workers) as p:
         p.run([(a, b, out)])
     return out

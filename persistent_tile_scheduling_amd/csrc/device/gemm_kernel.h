@@ -95,10 +95,9 @@ enum : int {
     SYNC_MERGED = 2   // per stage: full for A, full for B, one empty (3 words per stage)
 };
 
-// LOAD_PATH: how a ring stage is filled.
+// LOAD_PATH: how a ring stage is filled (one path is built).
 enum : int {
-    LOAD_DMA = 0, // global -> LDS loads (buffer_load ... lds), no registers
-    LOAD_REG = 1  // global -> registers one k-tile ahead, then ds_write
+    LOAD_DMA = 0 // global -> LDS loads (buffer_load ... lds), no registers
 };
 
 // The matrix instruction: a 32x32 output block per 16-deep k-step, or a 16x16
@@ -374,10 +373,8 @@ struct Mainloop {
     {
         kt0 = t.kt0;
         nk_all = t.nk;
-        a_tile = t.a + (int64_t)t.row0 * t.lda;
-        b_tile = t.b + (int64_t)t.col0 * t.ldb;
-        a_rsrc = buffer_rsrc(a_tile);
-        b_rsrc = buffer_rsrc(b_tile);
+        a_rsrc = buffer_rsrc(t.a + (int64_t)t.row0 * t.lda);
+        b_rsrc = buffer_rsrc(t.b + (int64_t)t.col0 * t.ldb);
         full_tile = t.vm == C::BM && t.vn == C::BN;
         a_shift = (uint32_t)(4 * C::A_LOADS * C::ROWS_PER_LOAD * t.lda * 2);
         b_shift = (uint32_t)(4 * C::B_LOADS * C::ROWS_PER_LOAD * t.ldb * 2);
@@ -571,30 +568,6 @@ struct Mainloop {
                 acc[mi][ni] = C::Op::run(f.b[ni], f.a[mi], acc[mi][ni]);
     }
 
-    // The MFMAs of one k-step with loads [first, first + count) of k-tile
-    // dma_kt issued between them, one load after every MFMAS/count MFMAs, so
-    // the load instructions never stall the MFMA stream in one burst.
-    template <int COUNT>
-    __device__ __forceinline__ void mma_with_loads(const Frags &f, typename C::Acc (&acc)[C::MI][C::NI], bool dma, int first,
-                                                   int dma_kt, int dma_stage, const TileCtx<C> &t)
-    {
-        constexpr int MFMAS = C::MI * C::NI;
-        constexpr int EVERY = MFMAS / COUNT > 0 ? MFMAS / COUNT : 1;
-        const bool tail = is_tail(dma_kt, t.k);
-#pragma unroll
-        for (int x = 0; x < MFMAS; ++x) {
-            const int mi = x / C::NI, ni = x % C::NI;
-            acc[mi][ni] = C::Op::run(f.b[ni], f.a[mi], acc[mi][ni]);
-            if (x % EVERY == 0 && x / EVERY < COUNT && dma) {
-                const int i = first + x / EVERY;
-                if (tail)
-                    issue_one<true>(i, dma_kt, dma_stage, t.k);
-                else
-                    issue_one<false>(i, dma_kt, dma_stage, t.k);
-            }
-        }
-    }
-
     // Ask the scheduler to interleave the next k-step's fragment reads with
     // this k-step's MFMAs (one read after each MFMA, the rest of the MFMAs
     // after), so LDS latency hides behind matrix work.
@@ -734,11 +707,8 @@ struct Mainloop {
     template <class Hook>
     __device__ __forceinline__ void run(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI], Hook &&on_last_stage)
     {
-        if constexpr (C::LOAD_PATH == LOAD_REG)
-            run_regs(t, acc, on_last_stage);
-        else if constexpr (C::STAGES >= 3)
-            run_spread(t, acc, on_last_stage);
-        else if constexpr (C::MB == 16 && C::WAVES == 4)
+        static_assert(C::STAGES == 2 && C::LOAD_PATH == LOAD_DMA, "the built k loops use a two-stage ring");
+        if constexpr (C::MB == 16 && C::WAVES == 4)
             run_single(t, acc, on_last_stage);
         else if constexpr (C::MB == 16)
             run_burst_rolling(t, acc, on_last_stage);
@@ -988,149 +958,6 @@ struct Mainloop {
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     }
 
-    // ---- register path ----------------------------------------------------
-    // The wave's LOADS 16-byte chunks of one k-tile, held in registers
-    // between their global load and their LDS store.
-    u32x4 staged[C::LOADS];
-
-    const uint16_t *a_tile, *b_tile; // operand tile origins (register path)
-
-    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const uint16_t *base) const
-    {
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, -1, 0x00020000);
-    }
-
-    // Global load number i of k-tile kt into staged[i]. The chunk's k start
-    // is clamped to the last chunk inside the rows' readable extent, which
-    // changes nothing except in the k-tail tile (whose k >= K part is zeroed
-    // in LDS before it is read), so the same branch-free code serves every
-    // k-tile.
-    __device__ __forceinline__ void gload_one(int i, int kt, const TileCtx<C> &t)
-    {
-        const bool is_a = i < C::A_LOADS;
-        const int j = is_a ? i : i - C::A_LOADS;
-        const int nl = is_a ? C::A_LOADS : C::B_LOADS;
-        const int c = load_chunk(j, nl);
-        const int klast = ((t.k + 7) & ~7) - 8;
-        const uint32_t off = (is_a ? a_off[j] : b_off[j]) - c * 16 + min(phys(kt) * C::BK + c * 8, klast) * 2;
-        staged[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_of(is_a ? a_tile : b_tile), off, 0, 0);
-    }
-
-    // LDS store of staged[i] into ring stage `stage` (same layout as a
-    // global->LDS load: lane l's chunk at 16 l inside its 1 KiB block).
-    __device__ __forceinline__ void swrite_one(int i, int stage)
-    {
-        const bool is_a = i < C::A_LOADS;
-        const int j = is_a ? i : i - C::A_LOADS;
-        const int nl = is_a ? C::A_LOADS : C::B_LOADS;
-        const uint32_t region = is_a ? 0u : (uint32_t)C::A_BYTES;
-        const uint32_t wbase = opaque_s((uint32_t)(stage * C::STAGE_BYTES) + region + (uint32_t)(wave * nl * 1024));
-        *(u32x4 *)(smem + wbase + j * 1024 + lane * 16) = staged[i];
-    }
-
-    // One k-step's MFMAs with COUNT staged chunks handed on between them:
-    // chunk i is stored from its registers into `stage`, then the same
-    // registers receive chunk i of k-tile `kt` (ordered by the data
-    // dependency), so every chunk spends one whole k-tile in flight.
-    template <int COUNT>
-    __device__ __forceinline__ void mma_with_staging(const Frags &f, typename C::Acc (&acc)[C::MI][C::NI], int first,
-                                                     int stage, int kt, const TileCtx<C> &t)
-    {
-        constexpr int MFMAS = C::MI * C::NI;
-        constexpr int EVERY = MFMAS / COUNT > 0 ? MFMAS / COUNT : 1;
-#pragma unroll
-        for (int x = 0; x < MFMAS; ++x) {
-            const int mi = x / C::NI, ni = x % C::NI;
-            acc[mi][ni] = C::Op::run(f.b[ni], f.a[mi], acc[mi][ni]);
-            if (x % EVERY == 0 && x / EVERY < COUNT) {
-                const int i = first + x / EVERY;
-                swrite_one(i, stage);
-                gload_one(i, kt, t);
-            }
-        }
-    }
-
-    template <int KS>
-    __device__ __forceinline__ void regs_kstep_ops(const Frags &f, typename C::Acc (&acc)[C::MI][C::NI], int stage, int kt_load,
-                                                   const TileCtx<C> &t)
-    {
-        // staging happens in the k-steps [FIRST, KSTEPS-2]: all of them before
-        // the barrier that publishes the stage (the last k-step runs after it)
-        constexpr int HALF = C::KSTEPS / 2;
-        constexpr int FIRST = C::KSTEPS - 1 - HALF;
-        constexpr int PER_STEP = C::LOADS / HALF;
-        if constexpr (KS < FIRST || KS == C::KSTEPS - 1)
-            mma(f, acc);
-        else
-            mma_with_staging<PER_STEP>(f, acc, (KS - FIRST) * PER_STEP, stage ^ 1, kt_load, t);
-    }
-
-    template <int KS>
-    __device__ __forceinline__ void regs_steps(Frags (&f)[2], typename C::Acc (&acc)[C::MI][C::NI], int stage, int kt_load,
-                                               const TileCtx<C> &t)
-    {
-        if constexpr (KS + 1 < C::KSTEPS) {
-            load_frags(stage, KS + 1, f[(KS + 1) & 1]);
-            regs_kstep_ops<KS>(f[KS & 1], acc, stage, kt_load, t);
-            interleave_reads_with_mfma();
-            regs_steps<KS + 1>(f, acc, stage, kt_load, t);
-        }
-    }
-
-    // Two LDS stages and one register stage. During the middle k-steps of
-    // k-tile kt (reading stage kt%2) each staged chunk of k-tile kt+1 (loaded
-    // during the same k-steps of kt-1) is stored into the other stage, which
-    // every wave left at the barrier that ended kt-1, and its registers then
-    // receive the chunk of k-tile kt+2. One barrier per k-tile publishes the
-    // stores. Past the last k-tile the loads re-read k-tile nk-1 and the
-    // stores go to a stage that is not read again, which keeps the loop free
-    // of branches.
-    template <class Hook>
-    __device__ __forceinline__ void run_regs(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI], Hook &on_last_stage)
-    {
-        static_assert(C::STAGES == 2, "register path uses two LDS stages");
-        static_assert(C::KSTEPS >= 3 && C::KSTEPS % 2 == 0 && C::LOADS % (C::KSTEPS / 2) == 0, "staging split");
-        const int nk = t.nk;
-        if (nk == 0) {
-            on_last_stage();
-            return;
-        }
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i)
-            gload_one(i, 0, t);
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i)
-            swrite_one(i, 0);
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i)
-            gload_one(i, min(1, nk - 1), t);
-        // the loop's first k-tile is the partial last one whenever the tile's
-        // rotated k order starts there
-        if (is_tail(0, t.k)) {
-            wait_lgkmcnt0();
-            zero_k_tail(0, 0, t.k);
-        }
-        barrier_lds();
-        Frags f[2];
-        load_frags(0, 0, f[0]);
-        for (int kt = 0; kt < nk; ++kt) {
-            const int stage = kt & 1;
-            const int kt_load = min(kt + 2, nk - 1);
-            regs_steps<0>(f, acc, stage, kt_load, t);
-            if (kt + 1 < nk) {
-                if (is_tail(kt + 1, t.k)) {
-                    wait_lgkmcnt0();
-                    zero_k_tail(kt + 1, stage ^ 1, t.k);
-                }
-                barrier_lds();
-                load_frags(stage ^ 1, 0, f[C::KSTEPS & 1]);
-            }
-            regs_kstep_ops<C::KSTEPS - 1>(f[(C::KSTEPS - 1) & 1], acc, stage, kt_load, t);
-        }
-        // the staging loads run to the end of the loop
-        on_last_stage();
-    }
-
     // ---- global->LDS path -------------------------------------------------
     // Two stages: the loads of k-tile kt+2 can only start once every wave has
     // left stage kt, i.e. at the barrier that ends k-tile kt; they are issued
@@ -1174,82 +1001,6 @@ struct Mainloop {
             // one MFMA site for the last k-step keeps the accumulators in one
             // register class across the loop
             mma(f[(C::KSTEPS - 1) & 1], acc);
-        }
-    }
-
-    // Three or more stages: the stage that k-tile kt used is free from the
-    // barrier that ends kt, and k-tile kt+STAGES goes into it; its loads are
-    // spread over the MFMAs of k-tile kt+1 (LOADS/KSTEPS per k-step), so they
-    // land STAGES-2 k-tiles before they are read.
-    template <class Hook>
-    __device__ __forceinline__ void run_spread(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI], Hook &on_last_stage)
-    {
-        static_assert(C::LOADS % C::KSTEPS == 0, "loads split evenly over k-steps");
-        constexpr int PER_STEP = C::LOADS / C::KSTEPS;
-        const int nk = t.nk;
-        if (nk == 0) {
-            on_last_stage();
-            return;
-        }
-        const int pro = min(C::STAGES, nk);
-        for (int s = 0; s < pro; ++s)
-            issue_any(s, s, t.k, nk);
-        // k-tile 0: its loads were the oldest of the prologue
-        wait_stage_loads<C, C::STAGES - 1>(min(C::STAGES - 1, nk - 1));
-        // the loop's first k-tile is the partial last one whenever the tile's
-        // rotated k order starts there
-        if (is_tail(0, t.k))
-            zero_k_tail(0, 0, t.k);
-        barrier_lds();
-        if (nk == 1)
-            on_last_stage();
-        Frags f[2];
-        load_frags(0, 0, f[0]);
-        for (int kt = 0; kt < nk; ++kt) {
-            const int stage = kt % C::STAGES;
-            // loads of k-tile kt + STAGES - 1 into the stage freed by kt - 1
-            const int dma_kt = kt + C::STAGES - 1;
-            const bool dma = kt >= 1 && dma_kt < nk;
-            const int dma_stage = (kt + C::STAGES - 1) % C::STAGES;
-#pragma unroll
-            for (int ks = 0; ks + 1 < C::KSTEPS; ++ks) {
-                load_frags(stage, ks + 1, f[(ks + 1) & 1]);
-                mma_with_loads<PER_STEP>(f[ks & 1], acc, dma, ks * PER_STEP, dma_kt, dma_stage, t);
-                interleave_reads_with_mfma();
-            }
-            if (kt + 1 < nk) {
-                // loads of k-tile kt+1 landed when at most the later issued
-                // k-tiles remain: kt+2 .. min(kt+STAGES-1, nk-1), counting the
-                // slice of kt+STAGES-1 still to come in this k-tile's last step
-                if (dma)
-                    wait_stage_loads_partial<C::STAGES - 3, PER_STEP * (C::KSTEPS - 1)>(
-                        min(C::STAGES - 3, nk - 1 - (kt + 2)));
-                else
-                    wait_stage_loads<C, C::STAGES - 2>(min(C::STAGES - 2, nk - 1 - (kt + 1)));
-                if (is_tail(kt + 1, t.k))
-                    zero_k_tail(kt + 1, (kt + 1) % C::STAGES, t.k);
-                barrier_lds();
-                if (kt + 2 == nk)
-                    on_last_stage();
-                load_frags((kt + 1) % C::STAGES, 0, f[C::KSTEPS & 1]);
-            }
-            mma_with_loads<PER_STEP>(f[(C::KSTEPS - 1) & 1], acc, dma, (C::KSTEPS - 1) * PER_STEP, dma_kt, dma_stage,
-                                     t);
-        }
-    }
-
-    // vmcnt for: `full` whole k-tiles of loads plus `extra` loads younger
-    // than the k-tile being waited for.
-    template <int N, int EXTRA>
-    __device__ __forceinline__ void wait_stage_loads_partial(int full)
-    {
-        if constexpr (N <= 0) {
-            wait_vmcnt<EXTRA>();
-        } else {
-            if (full >= N)
-                wait_vmcnt<N * C::LOADS + EXTRA>();
-            else
-                wait_stage_loads_partial<N - 1, EXTRA>(full);
         }
     }
 };

@@ -67,24 +67,15 @@ const std::vector<KernelEntry> &kernel_table()
         // higher clock than the 32x32 one under the power limit).
         make_entry<256, 256, 64, 2, true, pts::LOAD_DMA, 2, 4, 16>(),
         make_entry<256, 256, 64, 2, false, pts::LOAD_DMA, 2, 4, 16>(),
-        make_entry<256, 256, 64, 2, true, pts::LOAD_DMA, 2, 4>(),
-        make_entry<256, 256, 64, 2, false, pts::LOAD_DMA, 2, 4>(),
-        make_entry<256, 256, 64, 2, true, pts::LOAD_REG, 2, 4>(),
-        make_entry<256, 256, 64, 2, false, pts::LOAD_REG, 2, 4>(),
-        make_entry<256, 256, 32, 4, true, pts::LOAD_DMA, 2, 4>(),
-        make_entry<256, 256, 32, 4, false, pts::LOAD_DMA, 2, 4>(),
-        make_entry<256, 256, 64, 2, true>(),  make_entry<256, 256, 64, 2, false>(),
+        // one wave per SIMD, 128x128 each (the hand-laid k loop)
         make_entry<256, 256, 64, 2, true, pts::LOAD_DMA, 2, 2, 16>(),
         make_entry<256, 256, 64, 2, false, pts::LOAD_DMA, 2, 2, 16>(),
-        make_entry<256, 256, 32, 4, true>(),  make_entry<256, 256, 32, 4, false>(),
-        make_entry<256, 256, 64, 2, true, pts::LOAD_REG>(), make_entry<256, 256, 64, 2, false, pts::LOAD_REG>(),
         // 256x128: the default kernel on half the columns, its 8 waves as 4x2
         // (64x64 each: fewer fragment reads per MFMA than 2x4's 128x32, +5%
         // at 8192^3), for problems with too few 256x256 tiles
         make_entry<256, 128, 64, 2, true, pts::LOAD_DMA, 4, 2, 16>(),
         make_entry<256, 128, 64, 2, false, pts::LOAD_DMA, 4, 2, 16>(),
         make_entry<128, 128, 64, 2, true>(),  make_entry<128, 128, 64, 2, false>(),
-        make_entry<128, 128, 32, 4, true>(),  make_entry<128, 128, 32, 4, false>(),
         make_entry<64, 64, 64, 2, true>(),    make_entry<64, 64, 64, 2, false>(),
         // the default kernel with the stage hand-off through LDS arrive counters
         make_entry<256, 256, 64, 2, true, pts::LOAD_DMA, 2, 4, 16, pts::SYNC_FUSED>(),
@@ -99,11 +90,14 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 } // namespace
 
-struct gemm_plan {
+// Everything a run needs except device memory: built and validated on the
+// host by build_core, which allocates nothing on the device.
+struct PlanCore {
     int device = 0;
     int32_t group_count = 0;
-    std::vector<gemm_shape> shapes; // ld values resolved, in tile order
-    std::vector<int32_t> order;     // tile-order slot -> descriptor problem index
+    gemm_shape shapes[GEMM_MAX_GROUPS];       // ld values resolved, in tile order
+    int32_t order[GEMM_MAX_GROUPS];           // tile-order slot -> descriptor problem index
+    pts::GroupDesc groups[GEMM_MAX_GROUPS];   // the device table's contents, in tile order
     int32_t dtype_d = GEMM_DTYPE_F32;
     int32_t schedule = GEMM_SCHEDULE_STATIC;
     int32_t round = 0;
@@ -112,35 +106,25 @@ struct gemm_plan {
     KernelEntry kernel{};
     int64_t total_tiles = 0;
     int32_t workers = 0;
+};
+
+struct gemm_plan {
+    PlanCore core;
+    void *d_mem = nullptr;                  // the one device allocation (counters, then the group table)
     pts::GroupDesc *d_groups = nullptr;
     uint32_t *d_counters = nullptr;
     void *trace = nullptr;
     size_t trace_bytes = 0;
 };
 
-extern "C" {
-
-const char *gemm_status_string(gemm_status s)
-{
-    switch (s) {
-    case GEMM_OK: return "success";
-    case GEMM_ERR_INVALID_VALUE: return "invalid value";
-    case GEMM_ERR_UNSUPPORTED: return "unsupported configuration";
-    case GEMM_ERR_OUT_OF_MEMORY: return "out of device memory";
-    case GEMM_ERR_HIP: return "HIP runtime error";
-    case GEMM_ERR_TIMEOUT: return "device-side wait timed out";
-    }
-    return "unknown status";
-}
-
-const char *gemm_last_error(void) { return g_last_error.c_str(); }
+namespace {
 
 // Output tile for GEMM_TILE_AUTO: the first of 256x256, 256x128, 128x128
 // whose tile count (over all problems) reaches 55% of the compute units, else
 // 64x64. Larger tiles read less memory per flop, but a problem with too few of
 // them leaves most of the chip idle for the whole run; on bf16 squares from
 // 1024^3 to 6144^3 this rule picks the fastest of the four tiles.
-static void pick_auto_tile(const gemm_desc *desc, int cus, int &tm, int &tn)
+void pick_auto_tile(const gemm_desc *desc, int cus, int &tm, int &tn)
 {
     static const int cand[3][2] = {{256, 256}, {256, 128}, {128, 128}};
     for (const auto &c : cand) {
@@ -159,11 +143,11 @@ static void pick_auto_tile(const gemm_desc *desc, int cus, int &tm, int &tn)
     tm = tn = 64;
 }
 
-gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
+// Validate a descriptor and lay out its tile space (the plan's host part).
+// Allocates no device memory; needs the current HIP device for the compute
+// unit count and the kernel's occupancy.
+gemm_status build_core(const gemm_desc *desc, PlanCore &core)
 {
-    if (out_plan == nullptr)
-        return fail(GEMM_ERR_INVALID_VALUE, "out_plan is NULL");
-    *out_plan = nullptr;
     if (desc == nullptr)
         return fail(GEMM_ERR_INVALID_VALUE, "desc is NULL");
     if (desc->group_count < 1)
@@ -188,12 +172,11 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
         return fail(GEMM_ERR_INVALID_VALUE, "num_workers must be >= 0");
     if ((desc->flags & ~(GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED |
                          GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN | GEMM_FLAG_DEBUG_STAGE_FLAG_STALL)) != 0 ||
-        desc->flags == (GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED))
+        (desc->flags & (GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED)) ==
+            (GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED))
         return fail(GEMM_ERR_UNSUPPORTED, "unknown flags 0x%x (the two stage-flag layouts exclude each other)",
                     desc->flags);
     const uint32_t sync_flags = desc->flags & (GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED);
-    if (sync_flags == (GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED))
-        return fail(GEMM_ERR_UNSUPPORTED, "flags 0x%x: the two stage-flag layouts exclude each other", desc->flags);
     const int32_t sync = sync_flags == GEMM_FLAG_STAGE_FLAGS_FUSED    ? pts::SYNC_FUSED
                          : sync_flags == GEMM_FLAG_STAGE_FLAGS_MERGED ? pts::SYNC_MERGED
                                                                       : pts::SYNC_BARRIER;
@@ -204,31 +187,36 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
                       desc->load_path != 0 || desc->waves != 0 || desc->mfma != 0 || sync != pts::SYNC_BARRIER))
         return fail(GEMM_ERR_INVALID_VALUE,
                     "an automatic tile takes no other kernel choice (tile_m = tile_n = GEMM_TILE_AUTO, the rest 0)");
+    // the device is queried only once everything checkable without it has passed
+    int cus = 0;
+    auto query_device = [&]() -> hipError_t {
+        hipError_t qe = hipGetDevice(&core.device);
+        if (qe == hipSuccess)
+            qe = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, core.device);
+        return qe;
+    };
     int tm = desc->tile_m == 0 ? 256 : desc->tile_m;
     int tn = desc->tile_n == 0 ? 256 : desc->tile_n;
     if (auto_tile) {
-        int dev = 0, cus = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess)
-            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess)
-            return hip_fail(e, "querying the compute unit count");
+        const hipError_t qe = query_device();
+        if (qe != hipSuccess)
+            return hip_fail(qe, "querying the compute unit count");
         pick_auto_tile(desc, cus, tm, tn);
     }
     const bool out_bf16 = desc->dtype_d == GEMM_DTYPE_BF16;
     const KernelEntry *entry = nullptr;
-    if (desc->tile_k < 0 || desc->stages < 0 || desc->load_path < 0 || desc->load_path > 2 ||
+    if (desc->tile_k < 0 || desc->stages < 0 || desc->load_path < 0 || desc->load_path > 1 ||
         (desc->waves != 0 && desc->waves != 4 && desc->waves != 8) ||
         (desc->mfma != 0 && desc->mfma != 16 && desc->mfma != 32))
         return fail(GEMM_ERR_INVALID_VALUE,
-                    "tile_k and stages must be >= 0, load_path in 0..2, waves 0, 4 or 8, mfma 0, 16 or 32");
-    for (const KernelEntry &e : kernel_table())
-        if (e.bm == tm && e.bn == tn && e.out_bf16 == out_bf16 && (desc->tile_k == 0 || e.bk == desc->tile_k) &&
-            (desc->stages == 0 || e.stages == desc->stages) &&
-            (desc->load_path == 0 || e.load_path == desc->load_path - 1) &&
-            (desc->waves == 0 || e.waves == desc->waves) && (desc->mfma == 0 || e.mfma == desc->mfma) &&
-            e.sync == sync) {
-            entry = &e;
+                    "tile_k and stages must be >= 0, load_path 0 or 1, waves 0, 4 or 8, mfma 0, 16 or 32");
+    for (const KernelEntry &k : kernel_table())
+        if (k.bm == tm && k.bn == tn && k.out_bf16 == out_bf16 && (desc->tile_k == 0 || k.bk == desc->tile_k) &&
+            (desc->stages == 0 || k.stages == desc->stages) &&
+            (desc->load_path == 0 || k.load_path == desc->load_path - 1) &&
+            (desc->waves == 0 || k.waves == desc->waves) && (desc->mfma == 0 || k.mfma == desc->mfma) &&
+            k.sync == sync) {
+            entry = &k;
             break;
         }
     if (entry == nullptr && sync != pts::SYNC_BARRIER)
@@ -237,44 +225,33 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
         return fail(GEMM_ERR_UNSUPPORTED, "tile %dx%d (k %d, %d stages, load path %d, %d waves, mfma %d) is not built",
                     tm, tn, desc->tile_k, desc->stages, desc->load_path, desc->waves, desc->mfma);
 
-    auto plan = new (std::nothrow) gemm_plan();
-    if (plan == nullptr)
-        return fail(GEMM_ERR_OUT_OF_MEMORY, "host allocation failed");
-    std::vector<pts::GroupDesc> groups(desc->group_count);
-    std::vector<gemm_shape> shapes(desc->group_count);
+    pts::GroupDesc groups[GEMM_MAX_GROUPS];
+    gemm_shape shapes[GEMM_MAX_GROUPS];
     int64_t tiles = 0;
     for (int g = 0; g < desc->group_count; ++g) {
         gemm_shape s = desc->shapes[g];
-        if (s.m < 0 || s.n < 0 || s.k < 0 || s.m > INT32_MAX || s.n > INT32_MAX || s.k > INT32_MAX) {
-            delete plan;
+        if (s.m < 0 || s.n < 0 || s.k < 0 || s.m > INT32_MAX || s.n > INT32_MAX || s.k > INT32_MAX)
             return fail(GEMM_ERR_INVALID_VALUE, "problem %d: m, n, k must be in [0, 2^31)", g);
-        }
         if (s.lda == 0) s.lda = s.k;
         if (s.ldb == 0) s.ldb = s.k;
         if (s.ldd == 0) s.ldd = s.n;
-        if (s.lda < s.k || s.ldb < s.k || s.ldd < s.n || s.lda < 0 || s.ldb < 0 || s.ldd < 0) {
-            delete plan;
+        if (s.lda < s.k || s.ldb < s.k || s.ldd < s.n || s.lda < 0 || s.ldb < 0 || s.ldd < 0)
             return fail(GEMM_ERR_INVALID_VALUE, "problem %d: leading dimension smaller than the packed extent", g);
-        }
-        if ((s.lda % 8) != 0 || (s.ldb % 8) != 0) {
-            delete plan;
+        if ((s.lda % 8) != 0 || (s.ldb % 8) != 0)
             return fail(GEMM_ERR_INVALID_VALUE,
                         "problem %d: lda (%lld) and ldb (%lld) must be multiples of 8 elements (16-byte rows)", g,
                         (long long)s.lda, (long long)s.ldb);
-        }
         // load offsets inside one tile are 32-bit byte offsets from the tile's origin
         if ((int64_t)(tm - 1) * s.lda * 2 + (s.k + 8) * 2 >= ((int64_t)1 << 31) ||
-            (int64_t)(tn - 1) * s.ldb * 2 + (s.k + 8) * 2 >= ((int64_t)1 << 31)) {
-            delete plan;
+            (int64_t)(tn - 1) * s.ldb * 2 + (s.k + 8) * 2 >= ((int64_t)1 << 31))
             return fail(GEMM_ERR_UNSUPPORTED, "problem %d: lda/ldb too large for 32-bit tile offsets", g);
-        }
         shapes[g] = s;
         pts::GroupDesc &gd = groups[g];
         gd.m = (int32_t)s.m;
         gd.n = (int32_t)s.n;
         gd.k = (int32_t)s.k;
         gd.tiles_n = (int32_t)ceil_div(s.n, tn);
-        gd.tile_begin = (int32_t)tiles;
+        gd.tile_begin = 0;
         gd.num_k_tiles = (int32_t)ceil_div(s.k, entry->bk);
         gd.index = g;
         gd.pad1 = 0;
@@ -283,54 +260,39 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
         gd.ldd = s.ldd;
         if (s.m > 0 && s.n > 0)
             tiles += ceil_div(s.m, tm) * ceil_div(s.n, tn);
-        if (tiles >= (int64_t)1 << 27) {
-            delete plan;
+        if (tiles >= (int64_t)1 << 27)
             return fail(GEMM_ERR_UNSUPPORTED, "more than 2^27 output tiles");
-        }
     }
     // Tile order: deepest problems first (a tile's cost grows with its
     // k-tiles), so the long tiles start early and the short ones fill the end
     // of the run; the descriptor's order on request. Positions are then
-    // re-counted in that order.
-    std::vector<int32_t> order(desc->group_count);
+    // counted in that order (the prefix sums of "Schedules", section
+    // "Dynamic Domains").
+    core.group_count = desc->group_count;
     for (int g = 0; g < desc->group_count; ++g)
-        order[g] = g;
+        core.order[g] = g;
     if ((desc->flags & GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN) == 0)
-        std::stable_sort(order.begin(), order.end(),
+        std::stable_sort(core.order, core.order + desc->group_count,
                          [&](int32_t x, int32_t y) { return groups[x].num_k_tiles > groups[y].num_k_tiles; });
-    {
-        std::vector<pts::GroupDesc> sorted(desc->group_count);
-        int64_t begin = 0;
-        for (int i = 0; i < desc->group_count; ++i) {
-            sorted[i] = groups[order[i]];
-            sorted[i].tile_begin = (int32_t)begin;
-            const gemm_shape &s = shapes[order[i]];
-            if (s.m > 0 && s.n > 0)
-                begin += ceil_div(s.m, tm) * ceil_div(s.n, tn);
-            plan->shapes.push_back(s);
-        }
-        groups.swap(sorted);
+    int64_t begin = 0;
+    for (int i = 0; i < desc->group_count; ++i) {
+        const int32_t p = core.order[i];
+        core.groups[i] = groups[p];
+        core.groups[i].tile_begin = (int32_t)begin;
+        core.shapes[i] = shapes[p];
+        if (shapes[p].m > 0 && shapes[p].n > 0)
+            begin += ceil_div(shapes[p].m, tm) * ceil_div(shapes[p].n, tn);
     }
-    plan->order = order;
 
-    hipError_t e = hipGetDevice(&plan->device);
-    if (e != hipSuccess) {
-        delete plan;
-        return hip_fail(e, "hipGetDevice");
-    }
-    int cus = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, plan->device);
-    if (e != hipSuccess) {
-        delete plan;
-        return hip_fail(e, "hipDeviceGetAttribute");
-    }
+    hipError_t e = auto_tile ? hipSuccess : query_device();
+    if (e != hipSuccess)
+        return hip_fail(e, "querying the compute unit count");
     int occ = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, entry->fn, entry->waves * 64, 0);
-    if (e != hipSuccess || occ < 1) {
-        delete plan;
-        return e != hipSuccess ? hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor")
-                               : fail(GEMM_ERR_UNSUPPORTED, "kernel cannot be resident on this device");
-    }
+    if (e != hipSuccess)
+        return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    if (occ < 1)
+        return fail(GEMM_ERR_UNSUPPORTED, "kernel cannot be resident on this device");
     const int64_t resident = (int64_t)cus * occ;
     int64_t workers = desc->num_workers > 0 ? desc->num_workers : std::min<int64_t>(tiles, resident);
     int64_t round = workers;
@@ -340,46 +302,133 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
     }
     if (tiles == 0)
         workers = round = 0;
-    if (workers > 65535 * 16) {
-        delete plan;
+    if (workers > 65535 * 16)
         return fail(GEMM_ERR_INVALID_VALUE, "num_workers too large");
-    }
 
-    plan->group_count = desc->group_count;
-    plan->dtype_d = desc->dtype_d;
-    plan->schedule = desc->schedule;
-    plan->kernel = *entry;
-    plan->total_tiles = tiles;
-    plan->workers = (int32_t)workers;
-    plan->round = (int32_t)round;
+    core.dtype_d = desc->dtype_d;
+    core.schedule = desc->schedule;
+    core.kernel = *entry;
+    core.total_tiles = tiles;
+    core.workers = (int32_t)workers;
+    core.round = (int32_t)round;
     // Tile rows of a die's block start their k loops 2 k-tiles apart for runs
     // of up to 4 rounds of the resident workgroups (measured: +0.7-0.9% at 4
     // rounds; -2.5 to -4.6% for the dynamic schedules at 9 and 16, where the
     // workers of a die drift apart). A function of the problem set and the
     // device only, so every schedule and worker count sums in the same order.
-    plan->k_phase_row = tiles <= 4 * resident ? 2 : 0;
-    plan->full_excess = (desc->flags & GEMM_FLAG_DEBUG_STAGE_FLAG_STALL) != 0 ? 1 : 0;
+    core.k_phase_row = tiles <= 4 * resident ? 2 : 0;
+    core.full_excess = (desc->flags & GEMM_FLAG_DEBUG_STAGE_FLAG_STALL) != 0 ? 1 : 0;
+    return GEMM_OK;
+}
 
-    // counters first (4 KiB aligned blocks), then the group table
+// The kernel argument block of one run: per-run operand checks, then the
+// plan's values. `groups` and `counters` are the device table and counter
+// block the kernel reads.
+gemm_status fill_args(const PlanCore &core, const gemm_operands *ops, pts::GemmArgs &args)
+{
+    if (ops == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "ops is NULL");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev != core.device)
+        return fail(GEMM_ERR_INVALID_VALUE, "plan was created on device %d, current device is %d", core.device, dev);
+    memset(&args, 0, sizeof args);
+    const size_t esize_d = core.dtype_d == GEMM_DTYPE_BF16 ? 2 : 4;
+    for (int g = 0; g < core.group_count; ++g) {
+        // slot g of the tile order holds descriptor problem p
+        const int p = core.order[g];
+        const gemm_shape &s = core.shapes[g];
+        const gemm_operands &o = ops[p];
+        const bool has_tiles = s.m > 0 && s.n > 0;
+        if (has_tiles) {
+            if (o.d == nullptr || (s.k > 0 && (o.a == nullptr || o.b == nullptr)))
+                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: NULL operand pointer", p);
+            if (s.k > 0 && (((uintptr_t)o.a % 16) != 0 || ((uintptr_t)o.b % 16) != 0))
+                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: A and B must be 16-byte aligned", p);
+            if (((uintptr_t)o.d % esize_d) != 0)
+                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: D must be element aligned", p);
+        }
+        args.a[g] = (const uint16_t *)o.a;
+        args.b[g] = (const uint16_t *)o.b;
+        args.d[g] = o.d;
+        const size_t vec_bytes = 4 * esize_d;
+        if (((uintptr_t)o.d % vec_bytes) == 0 && ((size_t)s.ldd * esize_d) % vec_bytes == 0)
+            args.d_vec_ok |= (uint64_t)1 << g;
+    }
+    args.group_count = core.group_count;
+    args.total_tiles = (int32_t)core.total_tiles;
+    args.num_workers = core.workers;
+    args.schedule = core.schedule;
+    args.round = core.round;
+    args.full_excess = core.full_excess;
+    args.k_phase_row = core.k_phase_row;
+    return GEMM_OK;
+}
+
+gemm_status launch_gemm(const PlanCore &core, pts::GemmArgs &args, void *stream)
+{
+    void *kargs[] = {&args};
+    hipError_t e = hipLaunchKernel(core.kernel.fn, dim3(core.workers), dim3(core.kernel.waves * 64), kargs, 0,
+                                   (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipLaunchKernel");
+    return GEMM_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+const char *gemm_status_string(gemm_status s)
+{
+    switch (s) {
+    case GEMM_OK: return "success";
+    case GEMM_ERR_INVALID_VALUE: return "invalid value";
+    case GEMM_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GEMM_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case GEMM_ERR_HIP: return "HIP runtime error";
+    case GEMM_ERR_TIMEOUT: return "device-side wait timed out";
+    }
+    return "unknown status";
+}
+
+const char *gemm_last_error(void) { return g_last_error.c_str(); }
+
+gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan)
+{
+    if (out_plan == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "out_plan is NULL");
+    *out_plan = nullptr;
+    auto plan = new (std::nothrow) gemm_plan();
+    if (plan == nullptr)
+        return fail(GEMM_ERR_OUT_OF_MEMORY, "host allocation failed");
+    gemm_status st = build_core(desc, plan->core);
+    if (st != GEMM_OK) {
+        delete plan;
+        return st;
+    }
+    // one device block: the counters first (4 KiB aligned words), then the group table
     const size_t cbytes = sizeof(uint32_t) * pts::CTR_WORDS;
     static_assert(sizeof(uint32_t) * pts::CTR_WORDS == GEMM_SCHED_COUNTER_BYTES, "counter block size");
-    const size_t gbytes = sizeof(pts::GroupDesc) * groups.size();
-    void *mem = nullptr;
-    e = hipMalloc(&mem, cbytes + gbytes);
+    const size_t gbytes = sizeof(pts::GroupDesc) * plan->core.group_count;
+    hipError_t e = hipMalloc(&plan->d_mem, cbytes + gbytes);
     if (e != hipSuccess) {
+        plan->d_mem = nullptr;
         delete plan;
         (void)hipGetLastError();
         return fail(GEMM_ERR_OUT_OF_MEMORY, "hipMalloc of %zu bytes failed", cbytes + gbytes);
     }
-    plan->d_counters = (uint32_t *)mem;
-    plan->d_groups = (pts::GroupDesc *)((uint8_t *)mem + cbytes);
-    e = hipMemcpy(plan->d_groups, groups.data(), gbytes, hipMemcpyHostToDevice);
+    plan->d_counters = (uint32_t *)plan->d_mem;
+    plan->d_groups = (pts::GroupDesc *)((uint8_t *)plan->d_mem + cbytes);
+    e = hipMemcpy(plan->d_groups, plan->core.groups, gbytes, hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemset(plan->d_counters, 0, cbytes);
     if (e == hipSuccess)
         e = hipDeviceSynchronize();
     if (e != hipSuccess) {
-        (void)hipFree(mem);
+        (void)hipFree(plan->d_mem);
         delete plan;
         return hip_fail(e, "plan upload");
     }
@@ -392,8 +441,8 @@ gemm_status gemm_plan_destroy(gemm_plan *plan)
     if (plan == nullptr)
         return GEMM_OK;
     hipError_t e = hipSuccess;
-    if (plan->d_groups != nullptr)
-        e = hipFree(plan->d_groups);
+    if (plan->d_mem != nullptr)
+        e = hipFree(plan->d_mem); // the allocation's base address
     delete plan;
     return e == hipSuccess ? GEMM_OK : hip_fail(e, "hipFree");
 }
@@ -402,9 +451,9 @@ gemm_status gemm_plan_query(const gemm_plan *plan, int64_t *num_tiles, int32_t *
 {
     if (plan == nullptr)
         return fail(GEMM_ERR_INVALID_VALUE, "plan is NULL");
-    if (num_tiles) *num_tiles = plan->total_tiles;
-    if (num_workers) *num_workers = plan->workers;
-    if (lds_bytes) *lds_bytes = plan->kernel.lds_bytes + 8;
+    if (num_tiles) *num_tiles = plan->core.total_tiles;
+    if (num_workers) *num_workers = plan->core.workers;
+    if (lds_bytes) *lds_bytes = plan->core.kernel.lds_bytes + 8;
     return GEMM_OK;
 }
 
@@ -413,12 +462,12 @@ gemm_status gemm_plan_query_kernel(const gemm_plan *plan, int32_t *tile_m, int32
 {
     if (plan == nullptr)
         return fail(GEMM_ERR_INVALID_VALUE, "plan is NULL");
-    if (tile_m) *tile_m = plan->kernel.bm;
-    if (tile_n) *tile_n = plan->kernel.bn;
-    if (tile_k) *tile_k = plan->kernel.bk;
-    if (stages) *stages = plan->kernel.stages;
-    if (waves) *waves = plan->kernel.waves;
-    if (mfma) *mfma = plan->kernel.mfma;
+    if (tile_m) *tile_m = plan->core.kernel.bm;
+    if (tile_n) *tile_n = plan->core.kernel.bn;
+    if (tile_k) *tile_k = plan->core.kernel.bk;
+    if (stages) *stages = plan->core.kernel.stages;
+    if (waves) *waves = plan->core.kernel.waves;
+    if (mfma) *mfma = plan->core.kernel.mfma;
     return GEMM_OK;
 }
 
@@ -431,7 +480,8 @@ gemm_status gemm_plan_set_trace(gemm_plan *plan, void *device_buf, size_t bytes)
         plan->trace_bytes = 0;
         return GEMM_OK;
     }
-    const size_t need = sizeof(pts::TileTrace) * (size_t)plan->total_tiles + sizeof(pts::WorkerTrace) * plan->workers;
+    const size_t need =
+        sizeof(pts::TileTrace) * (size_t)plan->core.total_tiles + sizeof(pts::WorkerTrace) * plan->core.workers;
     if (bytes < need)
         return fail(GEMM_ERR_INVALID_VALUE, "trace buffer of %zu bytes; %zu needed", bytes, need);
     if (((uintptr_t)device_buf % 16) != 0)
@@ -467,62 +517,39 @@ gemm_status gemm_plan_read_counters(const gemm_plan *plan, uint32_t out[5])
     return GEMM_OK;
 }
 
+gemm_status gemm_plan_preset_claims(gemm_plan *plan, uint32_t value)
+{
+    if (plan == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "plan is NULL");
+    if (plan->core.schedule != GEMM_SCHEDULE_DYNAMIC && plan->core.schedule != GEMM_SCHEDULE_DYNAMIC_XCD)
+        return fail(GEMM_ERR_INVALID_VALUE, "only the dynamic schedules claim tiles");
+    if (value > 0x00FFFFFFu)
+        return fail(GEMM_ERR_INVALID_VALUE, "preset value must be below 2^24");
+    hipError_t e = hipDeviceSynchronize();
+    if (plan->core.schedule == GEMM_SCHEDULE_DYNAMIC) {
+        if (e == hipSuccess)
+            e = hipMemcpy(plan->d_counters + pts::CTR_CLAIM, &value, sizeof value, hipMemcpyHostToDevice);
+    } else {
+        for (int x = 0; x < pts::NUM_XCD && e == hipSuccess; ++x)
+            e = hipMemcpy(plan->d_counters + pts::ctr_xcd(x), &value, sizeof value, hipMemcpyHostToDevice);
+    }
+    return e == hipSuccess ? GEMM_OK : hip_fail(e, "presetting the claim counters");
+}
+
 gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream)
 {
     if (plan == nullptr)
         return fail(GEMM_ERR_INVALID_VALUE, "plan is NULL");
-    if (ops == nullptr)
-        return fail(GEMM_ERR_INVALID_VALUE, "ops is NULL");
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess)
-        return hip_fail(e, "hipGetDevice");
-    if (dev != plan->device)
-        return fail(GEMM_ERR_INVALID_VALUE, "plan was created on device %d, current device is %d", plan->device, dev);
-
     pts::GemmArgs args;
-    memset(&args, 0, sizeof args);
-    const size_t esize_d = plan->dtype_d == GEMM_DTYPE_BF16 ? 2 : 4;
-    for (int g = 0; g < plan->group_count; ++g) {
-        // slot g of the tile order holds descriptor problem p
-        const int p = plan->order[g];
-        const gemm_shape &s = plan->shapes[g];
-        const gemm_operands &o = ops[p];
-        const bool has_tiles = s.m > 0 && s.n > 0;
-        if (has_tiles) {
-            if (o.d == nullptr || (s.k > 0 && (o.a == nullptr || o.b == nullptr)))
-                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: NULL operand pointer", p);
-            if (s.k > 0 && (((uintptr_t)o.a % 16) != 0 || ((uintptr_t)o.b % 16) != 0))
-                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: A and B must be 16-byte aligned", p);
-            if (((uintptr_t)o.d % esize_d) != 0)
-                return fail(GEMM_ERR_INVALID_VALUE, "problem %d: D must be element aligned", p);
-        }
-        args.a[g] = (const uint16_t *)o.a;
-        args.b[g] = (const uint16_t *)o.b;
-        args.d[g] = o.d;
-        const size_t vec_bytes = 4 * esize_d;
-        if (((uintptr_t)o.d % vec_bytes) == 0 && ((size_t)s.ldd * esize_d) % vec_bytes == 0)
-            args.d_vec_ok |= (uint64_t)1 << g;
-    }
-    if (plan->workers == 0)
+    gemm_status st = fill_args(plan->core, ops, args);
+    if (st != GEMM_OK)
+        return st;
+    if (plan->core.workers == 0)
         return GEMM_OK;
     args.groups = plan->d_groups;
     args.counters = plan->d_counters;
     args.trace = (uint8_t *)plan->trace;
-    args.group_count = plan->group_count;
-    args.total_tiles = (int32_t)plan->total_tiles;
-    args.num_workers = plan->workers;
-    args.schedule = plan->schedule;
-    args.round = plan->round;
-    args.full_excess = plan->full_excess;
-    args.k_phase_row = plan->k_phase_row;
-
-    void *kargs[] = {&args};
-    e = hipLaunchKernel(plan->kernel.fn, dim3(plan->workers), dim3(plan->kernel.waves * 64), kargs, 0,
-                        (hipStream_t)stream);
-    if (e != hipSuccess)
-        return hip_fail(e, "hipLaunchKernel");
-    return GEMM_OK;
+    return launch_gemm(plan->core, args, stream);
 }
 
 gemm_status pts_copy_int16(const void *src, void *dst, int64_t n, int32_t num_blocks, void *stream)

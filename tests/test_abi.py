@@ -161,3 +161,13 @@ def test_tile_strings_other_than_auto_are_rejected(binding):
         binding.make_desc([(64, 64, 64)], tile="largest")
     d = binding.make_desc([(64, 64, 64)], tile="auto")
     assert (d.tile_m, d.tile_n) == (binding.GEMM_TILE_AUTO, binding.GEMM_TILE_AUTO)
+
+
+def test_gemm_convenience_checks_dtypes_before_anything_else(binding):
+    import torch
+    a = torch.zeros((8, 8), dtype=torch.float32)
+    b = torch.zeros((8, 8), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.gemm(a, b)
+    with pytest.raises(ValueError):
+        binding.gemm(b, b[0])

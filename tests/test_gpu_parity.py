@@ -4,9 +4,10 @@ Bars (the tolerance is written here, per case):
 * integer-valued inputs -- bit-exact: fp32 output equals the oracle's exact
   sum, bf16 output equals the oracle's round-to-nearest-even of it;
 * uniform[-1, 1] inputs -- max |D - ref| <= 2e-3 sqrt(K) (fp32 output) or
-  1e-2 sqrt(K) (bf16 output), over every element at oracle-sized shapes and
-  over sampled entries (every tile's four corners plus random entries) at the
-  full configuration sizes;
+  1e-2 sqrt(K) (bf16 output): over every element at oracle-sized shapes, over
+  every element of D for the 8192^3 and 5000x7000x3000 configurations, over
+  every element of every edge tile plus one full tile per problem for the
+  grouped configuration, and over 64 whole tiles of the 16384^2 x 8192 one;
 * static, dynamic, per-XCD dynamic and non-persistent schedules -- bitwise
   identical D (same tile body).
 """
@@ -75,9 +76,7 @@ SWEEP = [(1, 1, 1), (7, 7, 7), (63, 65, 64), (64, 64, 64), (65, 63, 65), (127, 1
 
 
 # every built kernel: (tile_m, tile_n, tile_k, stages, load path, waves[, mfma])
-KERNELS = [(64, 64, 64, 2, 1, 4), (128, 128, 64, 2, 1, 4), (128, 128, 32, 4, 1, 4), (256, 256, 64, 2, 1, 4),
-           (256, 256, 32, 4, 1, 4), (256, 256, 64, 2, 2, 4), (256, 256, 64, 2, 2, 8), (256, 256, 64, 2, 1, 8, 32),
-           (256, 256, 32, 4, 1, 8), (256, 256, 64, 2, 1, 8, 16), (256, 256, 64, 2, 1, 4, 16),
+KERNELS = [(64, 64, 64, 2, 1, 4), (128, 128, 64, 2, 1, 4), (256, 256, 64, 2, 1, 8, 16), (256, 256, 64, 2, 1, 4, 16),
            (256, 128, 64, 2, 1, 8, 16)]
 
 
@@ -156,10 +155,7 @@ def test_rotated_k_order_with_k_tail(pts, tile):
 @pytest.mark.parametrize("shape", [(600, 700, 300), (257, 129, 1000), (1000, 1000, 64), (513, 257, 2000),
                                    (40, 3000, 100)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("tile", [(256, 256, 64, 2, 1, 4), (256, 256, 32, 4, 1, 4), (256, 256, 64, 2, 2, 4),
-                                  (256, 256, 64, 2, 2, 8), (256, 256, 64, 2, 1, 8, 32), (256, 256, 32, 4, 1, 8),
-                                  (256, 256, 64, 2, 1, 8, 16), (256, 256, 64, 2, 1, 4, 16),
-                                  (256, 128, 64, 2, 1, 8, 16)])
+@pytest.mark.parametrize("tile", KERNELS)
 def test_random_ragged_full_oracle(pts, shape, out_dtype, tile):
     m, n, k = shape
     lda, ldb, ldd = _padded_ld(k) + 16, _padded_ld(k) + 8, n + 5
@@ -344,25 +340,37 @@ def test_grouped_variable_k_full_oracle(pts):
 
 
 # ---------------------------------------------------------------------------
-# Full-size configurations: sampled oracle entries + full fp32 property check
+# Full-size configurations: every element of D (8192^3, 5000x7000x3000) or of
+# whole tiles (grouped, 16384^2 x 8192) against the oracle
 # ---------------------------------------------------------------------------
 
+def _host_uniform(rows, cols, seed, tid, first_row=0):
+    """Rows first_row .. first_row+rows-1 of a (.. x cols) uniform operand, as bits."""
+    return gen.uniform_bf16_bits(seed, tid, rows * cols, start=first_row * cols).reshape(rows, cols)
+
+
 def _single_full(pts, m, n, k, out_dtype, seed=0):
-    a = U.device_uniform(m, k, seed, gen.TENSOR_A)
-    b = U.device_uniform(n, k, seed, gen.TENSOR_B)
-    (rows, cols), = U.sample_entries([(m, n)], 256, 256, 2048, seed=seed)
-    ref = U.oracle_sampled(seed, gen.TENSOR_A, gen.TENSOR_B, k, rows, cols)
-    outs = {}
+    """All four schedules, bitwise equal to each other; then every element of D
+    against the oracle's full product on the same seeded operands."""
+    a_bits = _host_uniform(m, k, seed, gen.TENSOR_A)
+    b_bits = _host_uniform(n, k, seed, gen.TENSOR_B)
+    a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
+    first = None
     for sched in SCHEDULES:
         U.log(f"full {m}x{n}x{k} {out_dtype} {sched}")
         d, counters, (tiles, workers) = U.run_single(m, n, k, a, b, out_dtype, sched)
-        err = U.check_sampled(d, rows, cols, ref, k, f"{m}x{n}x{k} {sched}")
-        U.log(f"  sampled max err {err:.3g} (tol {U.tol_for(out_dtype, k):.3g}), tiles {tiles} workers {workers}")
         U.check_counters(sched, counters, tiles, workers)
-        outs[sched] = d
-    for sched in SCHEDULES[1:]:
-        assert torch.equal(outs["static"], outs[sched])
-    U.check_against_fp32_matmul(outs["dynamic"], a, b, k, f"{m}x{n}x{k}")
+        if first is None:
+            first = d
+        else:
+            assert torch.equal(first, d), f"{sched} differs from static"
+            del d
+    U.check_against_fp32_matmul(first, a, b, k, f"{m}x{n}x{k}")
+    del a, b
+    U.log(f"  oracle: full {m}x{n}x{k} product on {oracle.max_threads()} host threads")
+    ref = oracle.gemm(a_bits, b_bits, m, n, k)
+    err = U.check_close(first, ref, k, f"{m}x{n}x{k} every element")
+    U.log(f"  every element: max |D - oracle| = {err:.3g} (tol {U.tol_for(out_dtype, k):.3g})")
 
 
 def test_generator_on_device_matches_host(pts):
@@ -370,16 +378,36 @@ def test_generator_on_device_matches_host(pts):
     assert np.array_equal(U.device_to_bits(t), gen.uniform_bf16_bits(0, gen.TENSOR_A, 1 << 20))
 
 
-def test_config2_8192_cube_bf16_sampled(pts):
+@pytest.mark.timeout(900)
+def test_config2_8192_cube_bf16_every_element(pts):
     _single_full(pts, 8192, 8192, 8192, torch.bfloat16)
 
 
-def test_config3_ragged_5000x7000x3000_fp32_sampled(pts):
+@pytest.mark.timeout(600)
+def test_config3_ragged_5000x7000x3000_fp32_every_element(pts):
     _single_full(pts, 5000, 7000, 3000, torch.float32)
 
 
-def test_config4_grouped_64_problems_sampled(pts):
-    seed, n, k = 0, 4096, 4096
+def _check_blocks(d, blocks, seed, a_tid, b_tid, k, what):
+    """Every element of each listed block (r0, r1, c0, c1) of D against the
+    oracle's product of A's rows r0..r1-1 and B's columns c0..c1-1 (regenerated
+    on the host from the same streams). Returns the largest error."""
+    worst = 0.0
+    for (r0, r1, c0, c1) in blocks:
+        a_rows = _host_uniform(r1 - r0, k, seed, a_tid, first_row=r0)
+        b_cols = _host_uniform(c1 - c0, k, seed, b_tid, first_row=c0)
+        ref = oracle.gemm(a_rows, b_cols, r1 - r0, c1 - c0, k)
+        worst = max(worst, U.check_close(d[r0:r1, c0:c1], ref, k, f"{what} block {(r0, r1, c0, c1)}"))
+    return worst
+
+
+@pytest.mark.timeout(600)
+def test_config4_grouped_64_problems_whole_tiles(pts):
+    """Every edge tile (the last tile row of each problem whose M_g is not a
+    multiple of 256, all 16 tile columns) and one full tile per problem (tile
+    column g mod 16 of the first full tile row), every element, against the
+    oracle."""
+    seed, n, k, bm, bn = 0, 4096, 4096, 256, 256
     ms = gen.grouped_m_draw(seed)
     shapes = [(m, n, k) for m in ms]
     tensors = []
@@ -387,26 +415,97 @@ def test_config4_grouped_64_problems_sampled(pts):
         ta, tb = gen.group_tensor_ids(g)
         tensors.append((U.device_uniform(m, k, seed, ta), U.device_uniform(n, k, seed, tb),
                         torch.empty((m, n), dtype=torch.bfloat16, device=U.DEV)))
-    samples = U.sample_entries([(m, n) for m in ms], 256, 256, 64, seed=1)
-    refs = []
-    for g, (rows, cols) in enumerate(samples):
-        ta, tb = gen.group_tensor_ids(g)
-        refs.append(U.oracle_sampled(seed, ta, tb, k, rows, cols))
-    outs = {}
+    first = None
     for sched in SCHEDULES:
         U.log(f"config4 grouped {sched} sum(M)={sum(ms)}")
         with pts.Plan(shapes, torch.bfloat16, schedule=sched) as p:
             p.run(tensors)
             torch.cuda.synchronize()
             U.check_counters(sched, p.counters(), p.num_tiles, p.num_workers)
-        worst = 0.0
-        for g, ((rows, cols), ref) in enumerate(zip(samples, refs)):
-            worst = max(worst, U.check_sampled(tensors[g][2], rows, cols, ref, k, f"config4 group {g} {sched}"))
-        U.log(f"  sampled max err {worst:.3g}")
-        outs[sched] = [t[2].clone() for t in tensors]
-    for sched in SCHEDULES[1:]:
-        for x, y in zip(outs["static"], outs[sched]):
-            assert torch.equal(x, y)
+        if first is None:
+            first = [t[2].clone() for t in tensors]
+        else:
+            for g, (x, t) in enumerate(zip(first, tensors)):
+                assert torch.equal(x, t[2]), f"{sched} differs from static in problem {g}"
+    del tensors
+    worst, edge_tiles, full_tiles = 0.0, 0, 0
+    for g, m in enumerate(ms):
+        ta, tb = gen.group_tensor_ids(g)
+        blocks = []
+        if m % bm:
+            r0 = m - m % bm
+            blocks.append((r0, m, 0, n))
+            edge_tiles += n // bn
+        if m >= bm:
+            c0 = (g % (n // bn)) * bn
+            blocks.append((0, bm, c0, c0 + bn))
+            full_tiles += 1
+        U.log(f"  oracle: problem {g} (M={m}) blocks {blocks}")
+        worst = max(worst, _check_blocks(first[g], blocks, seed, ta, tb, k, f"config4 problem {g}"))
+    U.log(f"  {edge_tiles} edge tiles and {full_tiles} full tiles, every element: max err {worst:.3g}")
+    assert full_tiles >= sum(1 for m in ms if m >= bm)
+
+
+def _raster_tile(pos, tiles_m, tiles_n, rows=8):
+    """The plan's tile order inside one problem (groups of `rows` tile rows,
+    each walked column by column): position -> (tile row, tile column)."""
+    group = pos // (rows * tiles_n)
+    first = group * rows
+    nrows = min(rows, tiles_m - first)
+    within = pos - first * tiles_n
+    return first + within % nrows, within // nrows
+
+
+@pytest.mark.timeout(600)
+def test_config5_with_concurrent_copy_whole_tiles(pts):
+    """16384^2 x 8192 while an int16 copy holds 64 CUs. 64 whole tiles are
+    compared with the oracle: 8 from each of the 8 classes of k-loop start
+    (position // 32 mod 8, one class per compute die's block of a round),
+    spread over the rounds and the tile rows of a raster group."""
+    m = n = 16384
+    k = 8192
+    seed = 0
+    bm = bn = 256
+    a = U.device_uniform(m, k, seed, gen.TENSOR_A)
+    b = U.device_uniform(n, k, seed, gen.TENSOR_B)
+    ncopy = 1 << 30
+    src = gen.uniform_bf16_torch(ncopy, seed, gen.TENSOR_COPY_SRC, U.DEV).view(torch.int16)
+    dst = torch.zeros(ncopy + 64, dtype=torch.int16, device=U.DEV)
+    # the copy holds 64 of the compute units while the GEMM runs
+    copy_stream = pts.pts_stream_create_cu_masked(64)
+    first = None
+    try:
+        for sched in SCHEDULES:
+            U.log(f"config5 {sched} with concurrent copy on 64 CUs")
+            dst.zero_()
+            d = torch.empty((m, n), dtype=torch.bfloat16, device=U.DEV)
+            torch.cuda.synchronize()
+            with pts.Plan([(m, n, k)], torch.bfloat16, schedule=sched) as p:
+                pts.pts_copy_int16(src, dst, ncopy, 256, copy_stream)
+                p.run([(a, b, d)])
+                torch.cuda.synchronize()
+            assert torch.equal(dst[:ncopy], src), "copy result differs"
+            assert torch.all(dst[ncopy:] == 0), "copy wrote past the end"
+            if first is None:
+                first = d
+            else:
+                assert torch.equal(first, d), f"{sched} differs from static"
+                del d
+    finally:
+        pts.pts_stream_destroy(copy_stream)
+    del a, b, src, dst
+    tiles_m, tiles_n = m // bm, n // bn
+    blocks, classes = [], set()
+    for c in range(8):
+        for s in range(8):
+            pos = 32 * (8 * ((3 * s + c) % 16) + c) + (5 * s + c) % 32
+            classes.add((pos // 32) % 8)
+            tm, tn = _raster_tile(pos, tiles_m, tiles_n)
+            blocks.append((tm * bm, tm * bm + bm, tn * bn, tn * bn + bn))
+    assert classes == set(range(8)) and len(set(blocks)) == 64
+    U.log(f"  oracle: 64 whole tiles of 256x256x{k}")
+    err = _check_blocks(first, blocks, seed, gen.TENSOR_A, gen.TENSOR_B, k, "config5")
+    U.log(f"  64 whole tiles: max err {err:.3g}")
 
 
 def test_config6_grouped_variable_k_sampled(pts):
@@ -438,35 +537,3 @@ def test_config6_grouped_variable_k_sampled(pts):
     for sched in SCHEDULES[1:]:
         for x, y in zip(outs["static"], outs[sched]):
             assert torch.equal(x, y)
-
-
-def test_config5_with_concurrent_copy_sampled(pts):
-    m = n = 16384
-    k = 8192
-    seed = 0
-    a = U.device_uniform(m, k, seed, gen.TENSOR_A)
-    b = U.device_uniform(n, k, seed, gen.TENSOR_B)
-    (rows, cols), = U.sample_entries([(m, n)], 256, 256, 2048, seed=2)
-    ref = U.oracle_sampled(seed, gen.TENSOR_A, gen.TENSOR_B, k, rows, cols)
-    ncopy = 1 << 30
-    src = gen.uniform_bf16_torch(ncopy, seed, gen.TENSOR_COPY_SRC, U.DEV).view(torch.int16)
-    dst = torch.zeros(ncopy + 64, dtype=torch.int16, device=U.DEV)
-    # the copy holds 64 of the compute units while the GEMM runs
-    copy_stream = pts.pts_stream_create_cu_masked(64)
-    outs = {}
-    for sched in SCHEDULES:
-        U.log(f"config5 {sched} with concurrent copy on 64 CUs")
-        dst.zero_()
-        d = torch.empty((m, n), dtype=torch.bfloat16, device=U.DEV)
-        torch.cuda.synchronize()
-        with pts.Plan([(m, n, k)], torch.bfloat16, schedule=sched) as p:
-            pts.pts_copy_int16(src, dst, ncopy, 256, copy_stream)
-            p.run([(a, b, d)])
-            torch.cuda.synchronize()
-        U.check_sampled(d, rows, cols, ref, k, f"config5 {sched}")
-        assert torch.equal(dst[:ncopy], src), "copy result differs"
-        assert torch.all(dst[ncopy:] == 0), "copy wrote past the end"
-        outs[sched] = d
-    pts.pts_stream_destroy(copy_stream)
-    for sched in SCHEDULES[1:]:
-        assert torch.equal(outs["static"], outs[sched])

@@ -256,3 +256,84 @@ def test_grouped_tile_order_deepest_first(pts, schedule, as_given):
     per_problem = 2 * 2   # 300 x 500 in 256 x 256 tiles
     order = list(range(len(ks))) if as_given else sorted(range(len(ks)), key=lambda g: -((ks[g] + 63) // 64))
     assert by_pos == [g for g in order for _ in range(per_problem)]
+
+
+def _preset_run(pts, schedule, preset, m=1000, n=1000, k=64):
+    """One traced run of an integer-valued problem with the claim counters
+    preset, D filled with NaN beforehand."""
+    a_bits = gen.operand_a(m, k, 17, kind="integer")
+    b_bits = gen.operand_b(k, n, 17, kind="integer")
+    ref = oracle.gemm(a_bits, b_bits, m, n, k)
+    a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
+    d = torch.full((m, n), float("nan"), dtype=torch.float32, device=U.DEV)
+    with pts.Plan([(m, n, k)], torch.float32, (256, 256), schedule) as p:
+        buf = torch.zeros(p.trace_bytes() // 4 + 4, dtype=torch.int32, device=U.DEV)
+        p.set_trace(buf)
+        p.preset_claims(preset)
+        p.run([(a, b, d)])
+        torch.cuda.synchronize()
+        tiles, workers = pts.decode_trace(buf, p.num_tiles, p.num_workers)
+        counters = p.counters()
+        nt, nw = p.num_tiles, p.num_workers
+    return d.cpu().double().numpy(), ref, tiles.copy(), workers.copy(), counters, nt, nw
+
+
+def test_claim_counter_preset_to_tile_count_writes_nothing(pts):
+    """The counter starts at T: every worker's first claim is the failed request
+    ("Advanced scheduling: Cluster Launch Control", section "One CLC request"),
+    so every worker leaves at once and D is untouched."""
+    d, _, _, workers, counters, nt, nw = _preset_run(pts, "dynamic", 16)
+    assert nt == 16
+    assert np.all(np.isnan(d)), "a tile was written although no claim succeeded"
+    assert workers["tiles"].tolist() == [0] * nw
+    # the preset T plus exactly one failed claim per worker; the counters reset
+    assert counters[:2] == [0, 0] and counters[2] == nt + nw
+
+
+def test_claim_counter_preset_to_k_writes_tiles_k_to_t(pts):
+    """The counter starts at k = 5: the run processes exactly the tile
+    positions 5 .. T-1, each once, and leaves the first five tiles unwritten."""
+    k0 = 5
+    d, ref, tiles, workers, counters, nt, nw = _preset_run(pts, "dynamic", k0)
+    ran = sorted(int(t) for t, w in zip(tiles["tile"], tiles["t_end"]) if w != 0)
+    assert ran == list(range(k0, nt))
+    assert int(workers["tiles"].sum()) == nt - k0
+    assert counters[2] == nt + nw          # k0 preset + (T - k0) tiles + one failed claim per worker
+    tiles_m = tiles_n = 4
+    for pos in range(nt):
+        tm, tn = pos % tiles_m, pos // tiles_m     # the plan's raster: 4 tile rows, walked by column
+        blk = d[tm * 256:(tm + 1) * 256, tn * 256:(tn + 1) * 256]
+        want = ref[tm * 256:(tm + 1) * 256, tn * 256:(tn + 1) * 256]
+        if pos < k0:
+            assert np.all(np.isnan(blk)), f"tile at position {pos} was written"
+        else:
+            assert np.array_equal(blk, want), f"tile at position {pos} is wrong"
+
+
+def test_xcd_claim_counters_preset_past_their_sequences_write_nothing(pts):
+    """Per-XCD counters preset beyond every XCD's sequence: each worker finds
+    its own sequence and every other one drained, and leaves at once."""
+    d, _, _, workers, counters, nt, nw = _preset_run(pts, "dynamic_xcd", 3)   # 16 tiles: 2 per XCD
+    assert np.all(np.isnan(d))
+    assert workers["tiles"].tolist() == [0] * nw
+    assert counters[:2] == [0, 0]
+
+
+def test_preset_claims_rejects_static_plans(pts):
+    with pts.Plan([(64, 64, 64)], torch.float32, (64, 64), "static") as p:
+        with pytest.raises(pts.GemmError):
+            p.preset_claims(1)
+
+
+def test_plans_created_and_destroyed_do_not_leak(pts):
+    """500 plans created and destroyed: the device's free memory comes back."""
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    free0, _ = torch.cuda.mem_get_info()
+    for i in range(500):
+        desc = pts.make_desc([(256 + i, 512, 64)] * (1 + i % 8), pts.GEMM_DTYPE_BF16,
+                             schedule=i % 3)
+        pts.gemm_plan_destroy(pts.gemm_plan_create(desc))
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 >= free0 - (2 << 20), f"free memory fell by {free0 - free1} bytes over 500 plans"
