@@ -278,6 +278,18 @@ def measured_traffic(workload_name, schedule, wl):
         return None
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's name."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(wl, budget_s: float):
     """The oracle on a bounded row sample of the workload's first problem."""
     import numpy as np
@@ -299,8 +311,53 @@ def cpu_baseline(wl, budget_s: float):
         rows = min(m, max(rows * 2, int(rows * budget_s / max(t, 1e-3))))
     flops = 2.0 * rows * n * k
     return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=oracle.max_threads(), kind="oracle",
-                seconds=t, sample=f"output rows 0..{rows - 1} (all {n} columns, K={k}) of problem 0, "
-                                  f"fp64 triple loop, OpenMP over rows")
+                cpu_model=cpu_model(), logical_cpus=os.cpu_count(), seconds=t,
+                sample=f"output rows 0..{rows - 1} (all {n} columns, K={k}) of problem 0, "
+                       f"fp64 i-k-j loop (each element summed k ascending), OpenMP over rows")
+
+
+IMBALANCED_SCHEDULES = ["static", "dynamic", "dynamic_xcd"]
+
+
+def imbalanced_comparison(pts, names, rounds, copy_cus):
+    """The workloads where dynamic claiming should matter (ragged, grouped,
+    concurrent copy): every schedule timed in interleaved rounds (medians of
+    HIP-event kernel times), then one traced run each for the tail-idle and
+    late-start fractions. Operands are freed before the next workload."""
+    import torch
+    out = {}
+    for name in names:
+        wl = workload(name)
+        wl["tile"] = tuple(wl["tile"][:2])
+        wl["flags"] = 0
+        ops = make_operands(wl)
+        conc = Concurrent(pts, wl["copy"], copy_cus) if wl["copy"] else None
+        torch.cuda.synchronize()
+        res = compare_schedules(pts, wl, ops, IMBALANCED_SCHEDULES, rounds, conc)
+        for sched in IMBALANCED_SCHEDULES:
+            res[sched].update(tail_idle(pts, wl, ops, sched, conc))
+        if conc is not None:
+            conc.close()
+        base = res["static"]["kernel_ms_median"]
+        entry = {
+            "workload": wl["desc"],
+            "tile": list(wl["tile"]),
+            "copy_cus": copy_cus if wl["copy"] else None,
+            "rounds": rounds,
+            "schedules": {s: {k: (round(v, 5) if isinstance(v, float) else v) for k, v in r.items()}
+                          for s, r in res.items()},
+            "dynamic_vs_static": {s: round(base / r["kernel_ms_median"], 4)
+                                  for s, r in res.items() if s != "static"},
+        }
+        out[name] = entry
+        print(f"# imbalanced {name}: " + ", ".join(
+            f"{s} {r['kernel_tflops_median']:.1f} TFLOP/s tail idle {r['tail_idle_frac']:.3f}"
+            for s, r in res.items()) + f"; dynamic/static {entry['dynamic_vs_static']}", file=sys.stderr,
+            flush=True)
+        del ops, conc
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -330,6 +387,10 @@ def main():
                     help="time only the vendor BLAS on the workload's operands (for side-by-side profiles)")
     ap.add_argument("--copy-cus", type=int, default=64,
                     help="compute units the concurrent copy may use (0 = all, unmasked stream)")
+    ap.add_argument("--imbalanced", default="c3,c4,c5",
+                    help="with the 8192^3 headline: also compare the schedules on these workloads ('' = skip)")
+    ap.add_argument("--imbalanced-rounds", type=int, default=7,
+                    help="interleaved rounds per schedule on each imbalanced workload")
     ap.add_argument("--calibration-copy", type=int, default=0,
                     help="also run one int16 copy of this many elements (PMC calibration)")
     args = ap.parse_args()
@@ -448,6 +509,12 @@ def main():
                                     "kernel_tflops_median": round(r["kernel_tflops_median"], 2)}
                                 for s, r in without_copy.items()}
         line["copy_alone_ms"] = round(copy_alone, 5)
+    if args.workload == "c2" and args.imbalanced and args.stage_sync == "barrier" and not any(
+            (args.tile_k, args.stages, args.load_path, args.waves, args.mfma)):
+        del ops
+        torch.cuda.empty_cache()
+        line["imbalanced"] = imbalanced_comparison(pts, args.imbalanced.split(","), args.imbalanced_rounds,
+                                                   args.copy_cus)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)

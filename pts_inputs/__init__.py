@@ -41,7 +41,7 @@ TENSOR_M_DRAW = 3
 TENSOR_K_DRAW = 4
 TENSOR_COPY_SRC = 5
 
-_CHUNK = 1 << 22
+_CHUNK = 1 << 18
 
 
 def group_tensor_ids(g: int) -> tuple[int, int]:
@@ -96,14 +96,34 @@ def _uniform_chunk(seed: int, tensor_id: int, count: int, start: int) -> np.ndar
     return f32_to_bf16_bits_rne(v)
 
 
+def _threads() -> int:
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
 def uniform_bf16_bits(seed: int, tensor_id: int, count: int, start: int = 0,
                       out: np.ndarray | None = None) -> np.ndarray:
-    """``count`` bf16 bit patterns of uniform[-1, 1) values, as uint16."""
+    """``count`` bf16 bit patterns of uniform[-1, 1) values, as uint16.
+
+    Each element depends only on its own stream index, so large requests are
+    split into chunks generated on several threads (numpy releases the GIL);
+    the values do not depend on the split.
+    """
     if out is None:
         out = np.empty(count, dtype=np.uint16)
-    for s in range(0, count, _CHUNK):
+
+    def fill(s):
         n = min(_CHUNK, count - s)
         out[s:s + n] = _uniform_chunk(seed, tensor_id, n, start + s)
+
+    starts = range(0, count, _CHUNK)
+    if count > 2 * _CHUNK and _threads() > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(_threads()) as pool:
+            list(pool.map(fill, starts))
+    else:
+        for s in starts:
+            fill(s)
     return out
 
 
