@@ -311,6 +311,31 @@ gemm_status gemm_plan_read_counters(const gemm_plan *plan, uint32_t out[5]);
  */
 gemm_status gemm_plan_preset_claims(gemm_plan *plan, uint32_t value);
 
+/* Bytes of the per-GPU scratch array gemm_run_noalloc uses (the claim counter
+ * block, then a table of GEMM_MAX_GROUPS problems). */
+#define GEMM_NOALLOC_SCRATCH_BYTES 40960
+
+/*
+ * gemm_run without a plan and without allocating, for callers that cannot
+ * call hipMalloc: code being recorded under HIP graph capture, tight serving
+ * loops, harnesses that forbid device allocation.
+ *
+ * `desc` is validated exactly as by gemm_plan_create (same errors, same
+ * tile, kernel and tile order) and `ops` / `stream` are as for gemm_run; the
+ * result is bit-identical to gemm_run of a plan built from the same `desc`.
+ * Instead of plan-owned memory the call uses a file-scope device array of
+ * GEMM_NOALLOC_SCRATCH_BYTES bytes, one per GPU, kept until the process ends:
+ * no hipMalloc, hipFree or other allocating call is made (the array's address
+ * is looked up once per device, on the first call there). Limits: at most
+ * GEMM_MAX_GROUPS problems (the scratch table's size; more give
+ * GEMM_ERR_UNSUPPORTED), no trace. Each call enqueues two kernels on `stream`:
+ * one that writes the problem table into the scratch and zeroes the claim
+ * counters, then the GEMM. Every call on a GPU shares that GPU's scratch, so
+ * calls that overlap on one GPU (two streams, or two host threads, without
+ * ordering between them) race and their results are void: order them.
+ */
+gemm_status gemm_run_noalloc(const gemm_desc *desc, const gemm_operands *ops, void *stream);
+
 /*
  * Grid-stride int16 copy dst[i] = src[i] for 0 <= i < n, 16 bytes per lane per
  * step ("Schedules", section "Domains": start = block * threads + thread,

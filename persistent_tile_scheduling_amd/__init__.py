@@ -35,6 +35,7 @@ GEMM_SCHEDULE_DYNAMIC_XCD = 2
 GEMM_SCHEDULE_NONPERSISTENT = 3
 GEMM_SCHED_COUNTER_BYTES = 36864
 GEMM_MAX_GROUPS = 64
+GEMM_NOALLOC_SCRATCH_BYTES = 40960
 GEMM_TILE_AUTO = -1
 GEMM_FLAG_NONE = 0
 GEMM_FLAG_STAGE_FLAGS_FUSED = 1
@@ -89,6 +90,7 @@ def _load():
         "gemm_plan_set_trace": (ctypes.c_int, [P, P, ctypes.c_size_t]),
         "gemm_plan_read_counters": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_uint32)]),
         "gemm_plan_preset_claims": (ctypes.c_int, [P, ctypes.c_uint32]),
+        "gemm_run_noalloc": (ctypes.c_int, [ctypes.POINTER(GemmDesc), ctypes.POINTER(GemmOperands), P]),
         "pts_copy_int16": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32, P]),
         "pts_stream_create_cu_masked": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(P)]),
         "pts_stream_destroy": (ctypes.c_int, [P]),
@@ -173,6 +175,15 @@ def gemm_run(plan: int, operands, stream=None) -> None:
     for i, (a, b, d) in enumerate(operands):
         arr[i] = GemmOperands(_ptr(a), _ptr(b), _ptr(d))
     _check(_lib.gemm_run(ctypes.c_void_p(plan), arr, ctypes.c_void_p(_stream_handle(stream))))
+
+
+def gemm_run_noalloc(desc: GemmDesc, operands, stream=None) -> None:
+    """gemm_run without a plan: validates ``desc`` and runs it using the
+    library's per-GPU scratch array (no device allocation)."""
+    arr = (GemmOperands * max(1, len(operands)))()
+    for i, (a, b, d) in enumerate(operands):
+        arr[i] = GemmOperands(_ptr(a), _ptr(b), _ptr(d))
+    _check(_lib.gemm_run_noalloc(ctypes.byref(desc), arr, ctypes.c_void_p(_stream_handle(stream))))
 
 
 def gemm_plan_destroy(plan: int | None) -> None:

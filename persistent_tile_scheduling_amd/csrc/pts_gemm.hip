@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -379,6 +380,83 @@ gemm_status launch_gemm(const PlanCore &core, pts::GemmArgs &args, void *stream)
 
 } // namespace
 
+// ---- the no-allocation entry point's scratch ---------------------------------
+// gemm_run_noalloc takes no plan: the device memory its kernels need beyond
+// the caller's operands (the claim counter block, then the problem table) is
+// this file-scope array, one copy per GPU, held until the process ends. Host
+// code never uses its name as an address: the per-device address comes from
+// hipGetSymbolAddress (scratch_address below).
+constexpr size_t NOALLOC_TABLE_OFFSET = GEMM_SCHED_COUNTER_BYTES;
+static_assert(NOALLOC_TABLE_OFFSET + sizeof(pts::GroupDesc) * GEMM_MAX_GROUPS <= GEMM_NOALLOC_SCRATCH_BYTES,
+              "scratch holds the counter block and a full problem table");
+static __device__ __align__(256) uint8_t scratch[GEMM_NOALLOC_SCRATCH_BYTES];
+
+// The setup kernel's argument block: the problem table travels by value.
+struct NoallocSetup {
+    pts::GroupDesc groups[GEMM_MAX_GROUPS];
+    uint8_t *scratch; // the device's scratch address
+    int32_t group_count;
+};
+static_assert(sizeof(NoallocSetup) <= 4096, "kernel argument block limit");
+
+// Writes the run's problem table into the scratch and zeroes the claim and
+// exit counters (they start each run at zero; the GEMM kernel also resets them
+// at its end, but a scratch shared by every call must not rely on the last
+// call having finished normally). Vector stores only.
+__global__ __launch_bounds__(64) void noalloc_setup_kernel(const NoallocSetup args_by_value)
+{
+    (void)args_by_value;
+    typedef const __attribute__((address_space(4))) NoallocSetup *Args;
+    const Args args = (Args)__builtin_amdgcn_kernarg_segment_ptr();
+    const int t = threadIdx.x;
+    uint8_t *const base = args->scratch;
+    uint32_t *const ctr = (uint32_t *)base;
+    pts::GroupDesc *const table = (pts::GroupDesc *)(base + NOALLOC_TABLE_OFFSET);
+    // the table as 32-bit words (a GroupDesc is 14 words)
+    typedef const __attribute__((address_space(4))) uint32_t *ArgWords;
+    static_assert(sizeof(pts::GroupDesc) % 4 == 0, "table of whole words");
+    const ArgWords src = (ArgWords)&args->groups[0];
+    uint32_t *const dst = (uint32_t *)table;
+    const int words = args->group_count * (int)(sizeof(pts::GroupDesc) / 4);
+    for (int i = t; i < words; i += 64)
+        dst[i] = src[i];
+    if (t == 0) {
+        ctr[pts::CTR_CLAIM] = 0u;
+        ctr[pts::CTR_EXIT] = 0u;
+    }
+    if (t < pts::NUM_XCD)
+        ctr[pts::ctr_xcd(t)] = 0u;
+}
+
+namespace {
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mutex;
+uint8_t *g_scratch_address[NOALLOC_MAX_DEVICES] = {};
+
+// The scratch array's address on `device`, which must be the current device:
+// looked up once per device (hipGetSymbolAddress), then kept.
+gemm_status scratch_address(int device, uint8_t **out)
+{
+    if (device < 0 || device >= NOALLOC_MAX_DEVICES)
+        return fail(GEMM_ERR_UNSUPPORTED, "device %d: gemm_run_noalloc serves devices 0..%d", device,
+                    NOALLOC_MAX_DEVICES - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_address[device] == nullptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_fail(e, "hipGetSymbolAddress of the scratch array");
+        if (p == nullptr || ((uintptr_t)p % 256) != 0)
+            return fail(GEMM_ERR_HIP, "scratch array at an unexpected address %p", p);
+        g_scratch_address[device] = (uint8_t *)p;
+    }
+    *out = g_scratch_address[device];
+    return GEMM_OK;
+}
+
+} // namespace
+
 extern "C" {
 
 const char *gemm_status_string(gemm_status s)
@@ -550,6 +628,42 @@ gemm_status gemm_run(gemm_plan *plan, const gemm_operands *ops, void *stream)
     args.counters = plan->d_counters;
     args.trace = (uint8_t *)plan->trace;
     return launch_gemm(plan->core, args, stream);
+}
+
+gemm_status gemm_run_noalloc(const gemm_desc *desc, const gemm_operands *ops, void *stream)
+{
+    if (desc != nullptr && desc->group_count > GEMM_MAX_GROUPS)
+        return fail(GEMM_ERR_UNSUPPORTED,
+                    "group_count %d: the scratch of gemm_run_noalloc holds a table of at most %d problems",
+                    desc->group_count, GEMM_MAX_GROUPS);
+    PlanCore core;
+    gemm_status st = build_core(desc, core);
+    if (st != GEMM_OK)
+        return st;
+    pts::GemmArgs args;
+    st = fill_args(core, ops, args);
+    if (st != GEMM_OK)
+        return st;
+    if (core.workers == 0)
+        return GEMM_OK;
+    uint8_t *base = nullptr;
+    st = scratch_address(core.device, &base);
+    if (st != GEMM_OK)
+        return st;
+    NoallocSetup setup;
+    memset(&setup, 0, sizeof setup);
+    memcpy(setup.groups, core.groups, sizeof(pts::GroupDesc) * core.group_count);
+    setup.scratch = base;
+    setup.group_count = core.group_count;
+    void *sargs[] = {&setup};
+    hipError_t e = hipLaunchKernel((const void *)&noalloc_setup_kernel, dim3(1), dim3(64), sargs, 0,
+                                   (hipStream_t)stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "setup kernel launch");
+    args.counters = (uint32_t *)base;
+    args.groups = (const pts::GroupDesc *)(base + NOALLOC_TABLE_OFFSET);
+    args.trace = nullptr;
+    return launch_gemm(core, args, stream);
 }
 
 gemm_status pts_copy_int16(const void *src, void *dst, int64_t n, int32_t num_blocks, void *stream)
