@@ -15,6 +15,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define PTS_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
+// Compile-time loop: f(IntC<0>{}), ..., f(IntC<N-1>{}), so each step can use
+// its index as a template argument (an instruction immediate).
+template <int I> struct IntC {
+    static constexpr int value = I;
+};
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(IntC<I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
 // s_waitcnt immediate for the gfx9 family: vmcnt[3:0] in bits 3:0, expcnt in
 // bits 6:4, lgkmcnt in bits 11:8, vmcnt[5:4] in bits 15:14. A field at its
 // maximum means "do not wait on this counter".
@@ -92,6 +106,18 @@ __device__ __forceinline__ void dma_load16(uint32_t lds_addr, uint32_t voff, u32
                  :
                  : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
                  : "memory");
+}
+
+// The same load with its LDS destination given as a scalar base plus a
+// compile-time byte offset, added straight into M0 (one instruction where a
+// copy and an add would otherwise precede the M0 write).
+template <int LDS_IMM>
+__device__ __forceinline__ void dma_load16_at(uint32_t lds_base, uint32_t voff, u32x4 rsrc, uint32_t soff)
+{
+    asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff), "i"(LDS_IMM)
+                 : "memory", "scc");
 }
 
 // The same load, performed only when `on` (a wave-uniform flag): with `on`

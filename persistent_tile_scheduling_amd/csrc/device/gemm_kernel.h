@@ -710,6 +710,8 @@ struct Mainloop {
         static_assert(C::STAGES == 2 && C::LOAD_PATH == LOAD_DMA, "the built k loops use a two-stage ring");
         if constexpr (C::MB == 16 && C::WAVES == 4)
             run_single(t, acc, on_last_stage);
+        else if constexpr (C::MB == 16 && C::SYNC == SYNC_BARRIER)
+            run_straight(t, acc, on_last_stage);
         else if constexpr (C::MB == 16)
             run_burst_rolling(t, acc, on_last_stage);
         else
@@ -861,6 +863,136 @@ struct Mainloop {
             rolling_step<(C::KSTEPS - 1) & 1>(f, acc, stage ^ 1, 0);
         }
         count_uses(nk);
+    }
+
+    // ---- the straightened k loop (8 waves, 16x16 blocks, barrier hand-off) ----
+    // The same k-tiles as run_burst_rolling, in the same order with the same
+    // loads, barriers and MFMAs, but a k-tile that needs nothing special -- its
+    // successor's stage is not the partial k-tile, it issues loads, and those
+    // loads are not the partial k-tile's -- runs a body with no test at all:
+    // k-step 0, the stage barrier, the loads of k-tile kt + 2, k-step 1. The
+    // few k-tiles that need more (the partial one's load and k-tail zeroing,
+    // the last two, where loads stop and the next claim goes out) take the
+    // general body. Full and edge tiles are separate instances, so the
+    // paired-load choice is fixed per instance.
+
+    // This wave's loads of k-tile kt into ring stage `stage`: the k-tile's
+    // byte offset is one scalar for all of them, each LDS destination the
+    // stage base plus a constant.
+    template <bool FULL>
+    __device__ __forceinline__ void issue_fast(int kt, int stage)
+    {
+        const uint32_t soff = (uint32_t)phys(kt) * (uint32_t)(C::BK * 2);
+        const uint32_t base = opaque_s(lds_address(smem) + (uint32_t)(stage * C::STAGE_BYTES));
+        if constexpr (FULL && PAIRED) {
+            if (wave < 4) {
+                const uint32_t a0 = base + (uint32_t)(wave * C::A_LOADS * 1024);
+                const uint32_t b0 = base + (uint32_t)(C::A_BYTES + wave * C::B_LOADS * 1024);
+                issue_set<0>(a0, a_off, a_rsrc, soff);
+                issue_set<0>(b0, b_off, b_rsrc, soff);
+                issue_set<4 * C::A_LOADS * 1024>(a0, a_off, a_rsrc, uniform((int)(soff + a_shift)));
+                issue_set<4 * C::B_LOADS * 1024>(b0, b_off, b_rsrc, uniform((int)(soff + b_shift)));
+            }
+        } else {
+            issue_set<0>(base + (uint32_t)(wave * C::A_LOADS * 1024), a_off, a_rsrc, soff);
+            issue_set<0>(base + (uint32_t)(C::A_BYTES + wave * C::B_LOADS * 1024), b_off, b_rsrc, soff);
+        }
+    }
+
+    template <int EXTRA, int N>
+    static __device__ __forceinline__ void issue_set(uint32_t lds_base, const uint32_t (&off)[N], u32x4 rsrc,
+                                                     uint32_t soff)
+    {
+        static_for<N>([&](auto j) {
+            constexpr int J = decltype(j)::value;
+            dma_load16_at<EXTRA + J * 1024>(lds_base, off[J], rsrc, soff);
+        });
+    }
+
+    // One k-tile with nothing special about it.
+    template <bool FULL>
+    __device__ __forceinline__ void straight_ktile(RollFrags &f, typename C::Acc (&acc)[C::MI][C::NI], int kt)
+    {
+        const int stage = kt & 1;
+        rolling_step<0>(f, acc, stage, 1);
+        // k-tile kt + 1's loads (this wave's) have landed; every wave is past
+        // its reads of stage kt
+        wait_vmcnt<0>();
+        barrier_lds();
+        issue_fast<FULL>(kt + 2, stage);
+        rolling_step<1>(f, acc, stage ^ 1, 0);
+    }
+
+    // One k-tile of the general body (the loop body of run_burst_rolling).
+    template <class Hook>
+    __device__ __forceinline__ void general_ktile(RollFrags &f, typename C::Acc (&acc)[C::MI][C::NI], int kt,
+                                                  const TileCtx<C> &t, Hook &on_last_stage)
+    {
+        const int nk = t.nk;
+        const int stage = kt & 1;
+        rolling_step<0>(f, acc, stage, 1);
+        if (kt + 1 < nk) {
+            stage_ready(kt + 1, t);
+            if (kt + 2 < nk)
+                issue_any(kt + 2, stage, t.k, nk);
+            if (kt + 2 == nk)
+                on_last_stage();
+        }
+        rolling_step<1>(f, acc, stage ^ 1, 0);
+    }
+
+    template <bool FULL, class Hook>
+    __device__ __forceinline__ void run_straight_t(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI],
+                                                   Hook &on_last_stage)
+    {
+        static_assert(C::KSTEPS == 2 && C::STAGES == 2, "two k-steps per k-tile, two stages");
+        const int nk = t.nk;
+        // the loop iteration whose k-tile is the partial last one (phys = nk - 1), or -1
+        const int tail_it = (t.k % C::BK) != 0 ? nk - 1 - kt0 : -1;
+        issue_any(0, 0, t.k, nk);
+        stage_ready(0, t);
+        if (1 < nk)
+            issue_any(1, 1, t.k, nk);
+        if (nk == 1)
+            on_last_stage();
+        RollFrags f;
+        read_all(0, 0, f, 0);
+        int kt = 0;
+        while (kt < nk) {
+            // straight k-tiles need kt + 2 < nk, kt + 2 != tail_it and kt + 1 != tail_it
+            int end = nk - 2;
+            if (kt <= tail_it - 2)
+                end = min(end, tail_it - 2);
+            else if (kt == tail_it - 1)
+                end = kt;
+            for (; kt < end; ++kt)
+                straight_ktile<FULL>(f, acc, kt);
+            if (kt >= nk)
+                break;
+            general_ktile(f, acc, kt, t, on_last_stage);
+            ++kt;
+        }
+    }
+
+    template <class Hook>
+    __device__ __forceinline__ void run_straight(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI],
+                                                 Hook &on_last_stage)
+    {
+        if (t.nk == 0) {
+            on_last_stage();
+            return;
+        }
+        // A wave whose whole wave tile lies outside the valid rows or columns of
+        // an edge tile computes nothing: it only loads and meets the stage
+        // barriers.
+        if (wm * C::WTM >= t.vm || wn * C::WTN >= t.vn) {
+            run_rolling_idle(t, on_last_stage);
+            return;
+        }
+        if (full_tile)
+            run_straight_t<true>(t, acc, on_last_stage);
+        else
+            run_straight_t<false>(t, acc, on_last_stage);
     }
 
     // ---- one wave per SIMD (16x16 blocks) ------------------------------------
