@@ -354,8 +354,8 @@ gemm_status fill_args(const PlanCore &core, const gemm_operands *ops, pts::GemmA
         args.a[g] = (const uint16_t *)o.a;
         args.b[g] = (const uint16_t *)o.b;
         args.d[g] = o.d;
-        const size_t vec_bytes = 4 * esize_d;
-        if (((uintptr_t)o.d % vec_bytes) == 0 && ((size_t)s.ldd * esize_d) % vec_bytes == 0)
+        // rows of D start 16-byte aligned: the epilogue may store whole 16-byte chunks
+        if (((uintptr_t)o.d % 16) == 0 && ((size_t)s.ldd * esize_d) % 16 == 0)
             args.d_vec_ok |= (uint64_t)1 << g;
     }
     args.group_count = core.group_count;
