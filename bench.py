@@ -360,6 +360,53 @@ def imbalanced_comparison(pts, names, rounds, copy_cus):
     return out
 
 
+def tile_cycle_fit(pts, schedule="static", ks=(1024, 2048, 4096, 8192), mn=8192):
+    """Shader cycles per tile against K (M = N = mn, bf16 out, 256x256 tiles):
+    from the kernel's own trace, the median tile (start of the tile to the end
+    of its epilogue) plus the median gap to the worker's next tile, fitted as
+    boundary + per_k_tile * (K / 64). The boundary is what a tile costs beyond
+    its k-tiles: decode, the first stage's load latency, the epilogue, the
+    hand-over to the next tile."""
+    import numpy as np
+    import pts_inputs as gen
+    import torch
+    rows = []
+    for k in ks:
+        a = gen.uniform_bf16_torch(mn * k, 0, gen.TENSOR_A, "cuda").view(mn, k)
+        b = gen.uniform_bf16_torch(mn * k, 0, gen.TENSOR_B, "cuda").view(mn, k)
+        d = torch.empty((mn, mn), dtype=torch.bfloat16, device="cuda")
+        with pts.Plan([(mn, mn, k)], torch.bfloat16, (256, 256), schedule) as p:
+            buf = torch.zeros(p.trace_bytes() // 4 + 4, dtype=torch.int32, device="cuda")
+            for _ in range(3):
+                p.run([(a, b, d)])
+            p.set_trace(buf)
+            tile_cyc, gaps, clocks = [], [], []
+            for _ in range(3):
+                p.run([(a, b, d)])
+                torch.cuda.synchronize()
+                tiles, _ = pts.decode_trace(buf, p.num_tiles, p.num_workers)
+                ns = (tiles["t_end"] - tiles["t_start"]).astype(np.float64) * 10.0
+                clock = tiles["cycles"].astype(np.float64).sum() / ns.sum()
+                order = np.lexsort((tiles["seq"], tiles["worker"]))
+                ts = tiles["t_start"][order].astype(np.float64)
+                te = tiles["t_end"][order].astype(np.float64)
+                same = tiles["worker"][order][1:] == tiles["worker"][order][:-1]
+                tile_cyc.append(float(np.median(tiles["cycles"].astype(np.float64))))
+                gaps.append(float(np.median((ts[1:] - te[:-1])[same] * 10.0 * clock)) if same.any() else 0.0)
+                clocks.append(clock)
+        rows.append(dict(k=k, k_tiles=k // 64, tile_cycles=float(np.median(tile_cyc)), gap_cycles=float(np.median(gaps)),
+                         clock_ghz=float(np.median(clocks))))
+        print(f"# K={k}: median tile {rows[-1]['tile_cycles']:.0f} cycles, gap to the next tile "
+              f"{rows[-1]['gap_cycles']:.0f}, clock {rows[-1]['clock_ghz']:.3f} GHz", file=sys.stderr, flush=True)
+        del a, b, d
+        torch.cuda.empty_cache()
+    x = np.array([r["k_tiles"] for r in rows], dtype=np.float64)
+    y = np.array([r["tile_cycles"] + r["gap_cycles"] for r in rows])
+    (b0, b1), *_ = np.linalg.lstsq(np.vstack([np.ones_like(x), x]).T, y, rcond=None)
+    return dict(schedule=schedule, mn=mn, rows=rows, boundary_cycles=float(b0), cycles_per_k_tile=float(b1),
+                mfma_ideal_cycles_per_k_tile=2048)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -391,6 +438,8 @@ def main():
                     help="with the 8192^3 headline: also compare the schedules on these workloads ('' = skip)")
     ap.add_argument("--imbalanced-rounds", type=int, default=7,
                     help="interleaved rounds per schedule on each imbalanced workload")
+    ap.add_argument("--tile-cycles", action="store_true",
+                    help="only fit shader cycles per tile against K (8192 x 8192 x K, K = 1024..8192) and print it")
     ap.add_argument("--calibration-copy", type=int, default=0,
                     help="also run one int16 copy of this many elements (PMC calibration)")
     args = ap.parse_args()
@@ -406,6 +455,10 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.tile_cycles:
+        fit = tile_cycle_fit(pts)
+        print(json.dumps({"tile_cycle_fit": fit}), flush=True)
+        return
     wl = workload(args.workload)
     wl["tile"] = tuple(wl["tile"][:2]) + (args.tile_k, args.stages, args.load_path, args.waves, args.mfma)
     wl["flags"] = {"barrier": 0, "fused": pts.GEMM_FLAG_STAGE_FLAGS_FUSED,
