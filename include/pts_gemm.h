@@ -13,8 +13,9 @@
  *     "Schedules", section "Scheduling Shapes".
  *   - dynamic work claiming: every tile, the first one included, is claimed
  *     from one device-wide atomic counter. The claim for the next tile is
- *     issued before the current tile is computed, and a claim that returns an
- *     index >= the tile count ends the worker's loop; it never claims again.
+ *     issued while the current tile is still being computed (once its last
+ *     ring stage is loaded), and a claim that returns an index >= the tile
+ *     count ends the worker's loop; it never claims again.
  *     This is the single-GPU analogue of the hardware work stealing in "Advanced
  *     scheduling: Cluster Launch Control", sections "One CLC request" and
  *     "Overlapping the request with the current computation".

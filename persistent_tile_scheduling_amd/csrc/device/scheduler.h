@@ -17,10 +17,13 @@
 // one device-scope atomic counter. Mapping the pages' CLC request onto it:
 //   * one lane issues the request (the pages: one thread submits try_cancel;
 //     several issuers would each take a coordinate);
-//   * the request for the next tile is issued before the current tile is
-//     computed and its result is read only after the tile, so the atomic's
-//     round trip hides behind the tile's work (section "Overlapping the
-//     request with the current computation");
+//   * the request for the next tile is issued while the current tile is being
+//     computed -- once its last ring stage is in LDS -- and its result is read
+//     only while the tile's accumulators are staged, so the atomic's round
+//     trip hides behind the last k-tile and the epilogue (section
+//     "Overlapping the request with the current computation"; issued at the
+//     tile's first k-tile instead, the round trip held up that tile's load
+//     waits, since vmcnt counts in issue order);
 //   * the result reaches the other waves through an LDS slot and a barrier,
 //     as the CLC response reaches the CTA through shared memory;
 //   * a claim returning an index >= T is the failed request: the worker
