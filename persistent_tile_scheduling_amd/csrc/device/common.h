@@ -120,6 +120,18 @@ __device__ __forceinline__ void dma_load16_at(uint32_t lds_base, uint32_t voff, 
                  : "memory", "scc");
 }
 
+// dma_load16_at with the byte offset as an argument: `lds_imm` must fold to a
+// constant by code generation (a literal, or the index of a fully unrolled
+// loop); the compiler rejects the statement otherwise.
+__device__ __forceinline__ void dma_load16_imm(uint32_t lds_base, int lds_imm, uint32_t voff, u32x4 rsrc,
+                                               uint32_t soff)
+{
+    asm volatile("s_add_u32 m0, %0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff), "i"(lds_imm)
+                 : "memory", "scc");
+}
+
 // The same load, performed only when `on` (a wave-uniform flag): with `on`
 // false the load runs with no lanes enabled, so it neither reads memory nor
 // writes LDS. Used where a branch around the load would cost more than the

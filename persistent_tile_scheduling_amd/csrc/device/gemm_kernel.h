@@ -339,12 +339,13 @@ struct Mainloop {
     uint32_t a_off[C::A_LOADS];
     uint32_t b_off[C::B_LOADS];
 
-    // logical k-chunk carried by this thread's i-th load (same for A and B)
-    __device__ __forceinline__ int load_chunk(int i, int nloads) const
+    // logical k-chunk carried by the i-th load of lane ln (same for A and B)
+    __device__ __forceinline__ int load_chunk(int i, int nloads, int ln) const
     {
-        const int r = (wave * nloads + i) * C::ROWS_PER_LOAD + lane / C::CHUNKS;
-        return (lane % C::CHUNKS) ^ lds_swizzle<C::BK>(r);
+        const int r = (wave * nloads + i) * C::ROWS_PER_LOAD + ln / C::CHUNKS;
+        return (ln % C::CHUNKS) ^ lds_swizzle<C::BK>(r);
     }
+    __device__ __forceinline__ int load_chunk(int i, int nloads) const { return load_chunk(i, nloads, lane); }
 
     // Paired loads (two waves per SIMD, two ring stages): on a full tile the
     // first wave of each SIMD issues its own loads and those of its partner
@@ -378,16 +379,20 @@ struct Mainloop {
         full_tile = t.vm == C::BM && t.vn == C::BN;
         a_shift = (uint32_t)(4 * C::A_LOADS * C::ROWS_PER_LOAD * t.lda * 2);
         b_shift = (uint32_t)(4 * C::B_LOADS * C::ROWS_PER_LOAD * t.ldb * 2);
-        const int rl = lane / C::CHUNKS;
+        // Rows and chunks from an index the compiler cannot see through: the
+        // per-lane values would otherwise be hoisted out of the tile loop and,
+        // live across every k loop, go to scratch.
+        const int ln = (int)opaque_v((uint32_t)lane);
+        const int rl = ln / C::CHUNKS;
 #pragma unroll
         for (int i = 0; i < C::A_LOADS; ++i) {
             const int r = (wave * C::A_LOADS + i) * C::ROWS_PER_LOAD + rl;
-            a_off[i] = (uint32_t)((int64_t)min(r, t.vm - 1) * t.lda * 2) + load_chunk(i, C::A_LOADS) * 16;
+            a_off[i] = (uint32_t)((int64_t)min(r, t.vm - 1) * t.lda * 2) + load_chunk(i, C::A_LOADS, ln) * 16;
         }
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i) {
             const int r = (wave * C::B_LOADS + i) * C::ROWS_PER_LOAD + rl;
-            b_off[i] = (uint32_t)((int64_t)min(r, t.vn - 1) * t.ldb * 2) + load_chunk(i, C::B_LOADS) * 16;
+            b_off[i] = (uint32_t)((int64_t)min(r, t.vn - 1) * t.ldb * 2) + load_chunk(i, C::B_LOADS, ln) * 16;
         }
         if constexpr (SINGLE) {
             // last 16-byte chunk start inside the rows' readable extent, as a
@@ -395,7 +400,7 @@ struct Mainloop {
             const int klast = ((t.k + 7) & ~7) - 8;
 #pragma unroll
             for (int p = 0; p < 2; ++p)
-                k_lim[p] = (klast - load_chunk(p, C::A_LOADS) * 8) * 2;
+                k_lim[p] = (klast - load_chunk(p, C::A_LOADS, ln) * 8) * 2;
         }
     }
 
@@ -1043,11 +1048,51 @@ struct Mainloop {
         }
     }
 
+    // The same k-step for a k-tile with nothing special about it (the loads,
+    // if any, are of a whole k-tile): the k-tile's byte offset is one scalar
+    // for all of this wave's loads and each LDS destination is the stage base
+    // plus a constant, so a load costs three instructions and no mask. One
+    // wave per SIMD issues at most one instruction per issue cycle, and the
+    // masked form's ten per load no longer fit between the MFMAs.
+    template <bool LOADS>
+    __device__ __forceinline__ void single_step_fast(const Frags &cur, Frags &nxt,
+                                                     typename C::Acc (&acc)[C::MI][C::NI], int rstage, int rks,
+                                                     uint32_t lbase, uint32_t soff)
+    {
+        static_assert(C::A_LOADS == C::B_LOADS, "A and B slots side by side");
+        const uint8_t *sa = a_base(rstage), *sb = b_base(rstage);
+        const uint32_t foff = frag_off[rks];
+#pragma unroll
+        for (int x = 0; x < S_MFMAS; ++x) {
+            const int mi = x / C::NI, ni = x % C::NI;
+            C::Op::run_fixed(cur.b[ni], cur.a[mi], acc[mi][ni]);
+            if (x % READ_EVERY == 0 && x / READ_EVERY < S_READS)
+                read_frag(nxt, x / READ_EVERY, sa, sb, foff);
+            if (LOADS && x % LOAD_EVERY == LOAD_EVERY - 1 && x / LOAD_EVERY < C::LOADS) {
+                const int i = x / LOAD_EVERY;
+                const bool is_a = i < C::A_LOADS;
+                const int j = is_a ? i : i - C::A_LOADS;
+                dma_load16_imm(lbase, (is_a ? 0 : C::A_BYTES) + j * 1024, is_a ? a_off[j] : b_off[j],
+                               is_a ? a_rsrc : b_rsrc, soff);
+            }
+        }
+    }
+
+    // LDS address of this wave's first A slot in `stage` (its B slots start
+    // A_BYTES further on).
+    __device__ __forceinline__ uint32_t single_lbase(int stage) const
+    {
+        return opaque_s(lds_address(smem) + (uint32_t)(stage * C::STAGE_BYTES + wave * C::A_LOADS * 1024));
+    }
+
     // Every k-tile has the same shape: k-step 0 (reading k-step 1), the
     // barrier that readies k-tile kt + 1, k-step 1 (reading k-step 0 of kt + 1
-    // and loading kt + 2). Past the end the reads fetch a stage nobody uses
-    // and the loads are masked off. With no branch around the MFMAs the
-    // accumulators stay in AGPRs for the whole loop.
+    // and loading kt + 2). A k-tile that needs nothing special -- kt + 2 < nk,
+    // and neither kt + 1 nor kt + 2 is the partial k-tile -- runs the straight
+    // form (no tests, unmasked loads); the others run the general form, where
+    // past the end the reads fetch a stage nobody uses and the loads are
+    // masked off. Both issue the same loads, barriers and MFMAs in the same
+    // order, so the result does not depend on which form ran.
     template <class Hook>
     __device__ __forceinline__ void run_single(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI],
                                                Hook &on_last_stage)
@@ -1075,7 +1120,26 @@ struct Mainloop {
             for (int ni = 0; ni < C::NI; ++ni)
                 asm volatile("" : "+a"(acc[mi][ni]));
         asm volatile("s_nop 4" ::: "memory");
-        for (int kt = 0; kt < nk; ++kt) {
+        // the loop iteration whose k-tile is the partial one (phys = nk - 1), or -1
+        const int tail_it = (t.k % C::BK) != 0 ? nk - 1 - kt0 : -1;
+        int kt = 0;
+        while (kt < nk) {
+            // straight k-tiles need kt + 2 < nk, kt + 2 != tail_it and kt + 1 != tail_it
+            int end = nk - 2;
+            if (kt <= tail_it - 2)
+                end = min(end, tail_it - 2);
+            else if (kt == tail_it - 1)
+                end = kt;
+            for (; kt < end; ++kt) {
+                const int stage = kt & 1;
+                single_step_fast<false>(f0, f1, acc, stage, 1, 0, 0);
+                wait_vmcnt<0>();
+                barrier_lds();
+                single_step_fast<true>(f1, f0, acc, stage ^ 1, 0, single_lbase(stage),
+                                       (uint32_t)phys(kt + 2) * (uint32_t)(C::BK * 2));
+            }
+            if (kt >= nk)
+                break;
             const int stage = kt & 1;
             single_step<false>(f0, f1, acc, stage, 1, 0, 0, false);
             if (kt + 1 < nk)
@@ -1083,6 +1147,7 @@ struct Mainloop {
             if (kt + 2 == nk)
                 on_last_stage();
             single_step<true>(f1, f0, acc, stage ^ 1, 0, kt + 2, stage, kt + 2 < nk);
+            ++kt;
         }
         // The accumulators were last written by MFMAs the compiler sees only
         // as assembly: leave the matrix unit's result latency before anything
@@ -1179,6 +1244,9 @@ __device__ __forceinline__ void store_epilogue(const TileCtx<C> &t, const typena
                                                int wm, int wn, int lane, int tid, uint8_t *smem, Hook &&on_staged)
 {
     using E = Epilogue<C>;
+    // per-tile addresses from opaque indices (see store_epilogue_wide)
+    lane = (int)opaque_v((uint32_t)lane);
+    tid = (int)opaque_v((uint32_t)tid);
     const int lr = lane % C::MB, lc = (lane / C::MB) * 4;
     constexpr int QS = C::MB * C::MB / 256; // 4-element groups per lane per block
     static_assert(sizeof(typename C::Acc) == QS * 16, "accumulator groups");
@@ -1306,7 +1374,9 @@ struct WideEpilogue {
     static constexpr int CHUNK = 16 / ES;                                // elements per 16-byte chunk
     static constexpr int CHUNKS_ROW = C::BN / CHUNK;
     static constexpr int ITERS = PASS_ROWS * CHUNKS_ROW / C::THREADS;    // chunks per thread per pass
-    static constexpr int BATCH = ITERS;  // every chunk read ahead of its store (8 at a time measured 1-3% slower)
+    // every chunk read ahead of its store (8 at a time measured 1-3% slower with
+    // two waves per SIMD); at most 16 (64 registers) at a time
+    static constexpr int BATCH = ITERS < 16 ? ITERS : 16;
     static constexpr int LDS_BYTES = PASS_ROWS * PITCH;
     static_assert(C::MB == 16 && C::MI % PASSES == 0, "16x16 blocks, passes split the row blocks");
     static_assert(PASS_ROWS * CHUNKS_ROW == ITERS * C::THREADS, "whole chunks per thread");
@@ -1321,6 +1391,12 @@ __device__ __forceinline__ void store_epilogue_wide(const TileCtx<C> &t, const t
                                                     Hook &&on_staged)
 {
     using E = WideEpilogue<C>;
+    // The thread's staging and store addresses are formed here, per tile,
+    // from indices the compiler cannot see through: hoisted out of the tile
+    // loop they would stay live across the k loop, where every register is
+    // taken, and go to scratch.
+    lane = (int)opaque_v((uint32_t)lane);
+    tid = (int)opaque_v((uint32_t)tid);
     const int lr = lane % 16, lc = (lane / 16) * 4;
     uint8_t *const tile_base = (uint8_t *)t.d + ((int64_t)t.row0 * t.ldd + t.col0) * E::ES;
     const bool full = t.vec_ok && t.vm == C::BM && t.vn == C::BN;
@@ -1346,6 +1422,9 @@ __device__ __forceinline__ void store_epilogue_wide(const TileCtx<C> &t, const t
                 } else {
                     *(f32x4 *)dst = f32x4{v[0], v[1], v[2], v[3]};
                 }
+                // one block at a time: accumulators held in AGPRs are read
+                // into VGPRs only as each block is staged
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         if (pass == 0)
