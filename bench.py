@@ -116,12 +116,34 @@ def copy_alone_ms(conc, runs):
     return ts[len(ts) // 2]
 
 
+LATE = "+claim_after_tile"
+
+
+def plan_args(pts, wl, key):
+    """(schedule, flags) of a comparison key: a schedule name, or a name with
+    the suffix '+claim_after_tile' (the same schedule with request-ahead off)."""
+    if key.endswith(LATE):
+        return key[:-len(LATE)], wl["flags"] | pts.GEMM_FLAG_CLAIM_AFTER_TILE
+    return key, wl["flags"]
+
+
+def claim_ahead_summary(results):
+    """Kernel time with request-ahead off over the time with it on, per
+    dynamic schedule (> 1: asking for the next tile early pays)."""
+    out = {}
+    for key, r in results.items():
+        if key.endswith(LATE) and key[:-len(LATE)] in results and "kernel_ms_median" in r:
+            out[key[:-len(LATE)]] = round(r["kernel_ms_median"] / results[key[:-len(LATE)]]["kernel_ms_median"], 4)
+    return out
+
+
 def time_headline(pts, wl, ops, schedule, steps, warmup, conc=None):
     """K timed steps of one schedule, wall clock plus per-launch HIP events."""
     import torch
     stream = torch.cuda.Stream()
     flops = sum(2.0 * m * n * k for (m, n, k) in wl["shapes"])
-    with pts.Plan(wl["shapes"], wl["out"], wl["tile"], schedule, 0, wl["flags"]) as plan:
+    sched, flags = plan_args(pts, wl, schedule)
+    with pts.Plan(wl["shapes"], wl["out"], wl["tile"], sched, 0, flags) as plan:
         for _ in range(warmup):
             if conc is not None:
                 conc.launch()
@@ -160,7 +182,10 @@ def compare_schedules(pts, wl, ops, schedules, rounds, conc=None):
     import torch
     stream = torch.cuda.Stream()
     flops = sum(2.0 * m * n * k for (m, n, k) in wl["shapes"])
-    plans = {s: pts.Plan(wl["shapes"], wl["out"], wl["tile"], s, 0, wl["flags"]) for s in schedules}
+    plans = {}
+    for s in schedules:
+        sched, flags = plan_args(pts, wl, s)
+        plans[s] = pts.Plan(wl["shapes"], wl["out"], wl["tile"], sched, 0, flags)
     times = {s: [] for s in schedules}
     try:
         for s in schedules:
@@ -194,7 +219,8 @@ def tail_idle(pts, wl, ops, schedule, conc=None):
     """Fraction of worker-time idle after each worker's last tile, from the trace."""
     import torch
     stream = torch.cuda.Stream()
-    with pts.Plan(wl["shapes"], wl["out"], wl["tile"], schedule, 0, wl["flags"]) as plan:
+    sched, flags = plan_args(pts, wl, schedule)
+    with pts.Plan(wl["shapes"], wl["out"], wl["tile"], sched, 0, flags) as plan:
         buf = torch.zeros(plan.trace_bytes() // 4 + 4, dtype=torch.int32, device="cuda")
         plan.set_trace(buf)
         for _ in range(2):
@@ -316,7 +342,7 @@ def cpu_baseline(wl, budget_s: float):
                        f"fp64 i-k-j loop (each element summed k ascending), OpenMP over rows")
 
 
-IMBALANCED_SCHEDULES = ["static", "dynamic", "dynamic_xcd"]
+IMBALANCED_SCHEDULES = ["static", "dynamic", "dynamic_xcd", "dynamic" + LATE, "dynamic_xcd" + LATE]
 
 
 def imbalanced_comparison(pts, names, rounds, copy_cus):
@@ -348,12 +374,13 @@ def imbalanced_comparison(pts, names, rounds, copy_cus):
                           for s, r in res.items()},
             "dynamic_vs_static": {s: round(base / r["kernel_ms_median"], 4)
                                   for s, r in res.items() if s != "static"},
+            "claim_ahead": claim_ahead_summary(res),
         }
         out[name] = entry
         print(f"# imbalanced {name}: " + ", ".join(
             f"{s} {r['kernel_tflops_median']:.1f} TFLOP/s tail idle {r['tail_idle_frac']:.3f}"
-            for s, r in res.items()) + f"; dynamic/static {entry['dynamic_vs_static']}", file=sys.stderr,
-            flush=True)
+            for s, r in res.items()) + f"; dynamic/static {entry['dynamic_vs_static']}; request-ahead off/on "
+            f"{entry['claim_ahead']}", file=sys.stderr, flush=True)
         del ops, conc
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
@@ -413,7 +440,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--schedules", default="static,dynamic,dynamic_xcd,nonpersistent")
+    ap.add_argument("--schedules", default="static,dynamic,dynamic_xcd,nonpersistent,dynamic_xcd" + LATE,
+                    help="comma list; a '+claim_after_tile' suffix turns the dynamic schedules' request-ahead off")
     ap.add_argument("--tile-k", type=int, default=0, help="k-tile depth (0 = library default)")
     ap.add_argument("--stages", type=int, default=0, help="LDS ring stages (0 = library default)")
     ap.add_argument("--load-path", type=int, default=0, help="1 = global->LDS, 2 = via registers (0 = default)")
@@ -557,6 +585,8 @@ def main():
     if "static" in results and "kernel_ms_median" in results["static"]:
         line["dynamic_vs_static"] = {s: round(results["static"]["kernel_ms_median"] / r["kernel_ms_median"], 4)
                                      for s, r in results.items() if s != "static" and "kernel_ms_median" in r}
+    if claim_ahead_summary(results):
+        line["claim_ahead"] = claim_ahead_summary(results)
     if without_copy:
         line["without_copy"] = {s: {"kernel_ms_median": round(r["kernel_ms_median"], 5),
                                     "kernel_tflops_median": round(r["kernel_tflops_median"], 2)}

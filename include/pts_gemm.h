@@ -137,6 +137,18 @@ typedef struct {
  * no more; the kernel ends and D is void. It shows that the waits are bounded.
  */
 #define GEMM_FLAG_DEBUG_STAGE_FLAG_STALL 8u
+/*
+ * Claim timing of the dynamic schedules (request-ahead off). By default a
+ * worker asks for its next tile once the current tile's last stage is in LDS,
+ * so the request's round trip overlaps the last k-tile and the epilogue (the
+ * Cluster Launch Control page, section on overlapping the request with the
+ * current computation). With this flag the request goes out only after the
+ * tile's epilogue and the worker waits for the answer before it starts the
+ * next tile: the baseline that shows what the overlap is worth. Results are
+ * identical; the static and non-persistent schedules issue no requests and
+ * ignore it.
+ */
+#define GEMM_FLAG_CLAIM_AFTER_TILE 16u
 
 /*
  * tile_m = tile_n = GEMM_TILE_AUTO: gemm_plan_create picks the output tile

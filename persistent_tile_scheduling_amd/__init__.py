@@ -42,6 +42,7 @@ GEMM_FLAG_STAGE_FLAGS_FUSED = 1
 GEMM_FLAG_STAGE_FLAGS_MERGED = 2
 GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN = 4
 GEMM_FLAG_DEBUG_STAGE_FLAG_STALL = 8
+GEMM_FLAG_CLAIM_AFTER_TILE = 16
 
 TILE_TRACE_BYTES = 56
 WORKER_TRACE_BYTES = 32

@@ -81,7 +81,7 @@ struct GemmArgs {
     int32_t round;     // static dealing width (see static_position)
     int32_t full_excess; // test only: added to every stage-flag full target (0 in normal runs)
     int32_t k_phase_row; // k-tiles between successive tile rows' k starts (see k_phase)
-    int32_t pad0;
+    int32_t claim_late;  // 1: the next tile is requested after this tile's epilogue, not before it
     uint64_t d_vec_ok; // bit g: problem g's D rows start 16-byte aligned (whole-chunk stores)
     const uint16_t *a[PTS_MAX_GROUPS];
     const uint16_t *b[PTS_MAX_GROUPS];
@@ -1525,6 +1525,8 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     const bool tracing = trace != nullptr;
     const uint64_t t_worker0 = tracing ? realtime() : 0;
 
+    // Request-ahead off (a measurement baseline): no claim before the epilogue.
+    const bool claim_late = args->claim_late != 0;
     Claimed cur = sched.first(tid);
     int seq = 0;
     while (cur.pos < total_tiles) {
@@ -1543,16 +1545,23 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
         // The request for the next tile goes out once this tile's last stage
         // is in LDS: its round trip overlaps the last k-tile and the epilogue,
         // and no load wait of this tile is held up by it.
-        ml.run(tc, acc, [&] { sched.claim_ahead(leader); });
+        ml.run(tc, acc, [&] {
+            if (!claim_late)
+                sched.claim_ahead(leader);
+        });
         // every wave has finished reading the ring before it is reused for staging
         barrier_raw();
         // The next tile's claim is resolved while the accumulators are staged
         // (its request went out a k-tile ago) and published by the staging
         // barrier, so no wave waits on it after the stores.
+        auto stage = [&] {
+            if (!claim_late)
+                sched.stage_next(tid, seq);
+        };
         if constexpr (WIDE_EPI)
-            store_epilogue_wide<C>(tc, acc, ml.wm, ml.wn, lane, tid, smem, [&] { sched.stage_next(tid, seq); });
+            store_epilogue_wide<C>(tc, acc, ml.wm, ml.wn, lane, tid, smem, stage);
         else
-            store_epilogue<C>(tc, acc, ml.wm, ml.wn, lane, tid, smem, [&] { sched.stage_next(tid, seq); });
+            store_epilogue<C>(tc, acc, ml.wm, ml.wn, lane, tid, smem, stage);
 
         if (tracing && leader) {
             TileTrace r;
@@ -1576,7 +1585,14 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
         // in every wave before the next tile's loads overwrite the ring.
         wait_lgkmcnt0();
         barrier_raw();
-        cur = sched.read_next(cur, seq);
+        if (claim_late) {
+            // ask only now, and wait for the answer (resolved and published
+            // through LDS with a barrier)
+            sched.claim_ahead(leader);
+            cur = sched.next(cur, tid, seq);
+        } else {
+            cur = sched.read_next(cur, seq);
+        }
         ++seq;
     }
 

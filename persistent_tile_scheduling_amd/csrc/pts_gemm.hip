@@ -104,6 +104,7 @@ struct PlanCore {
     int32_t round = 0;
     int32_t k_phase_row = 0; // k-tiles between tile rows' k starts in a die's block
     int32_t full_excess = 0; // test only (GEMM_FLAG_DEBUG_STAGE_FLAG_STALL)
+    int32_t claim_late = 0;  // GEMM_FLAG_CLAIM_AFTER_TILE
     KernelEntry kernel{};
     int64_t total_tiles = 0;
     int32_t workers = 0;
@@ -172,7 +173,8 @@ gemm_status build_core(const gemm_desc *desc, PlanCore &core)
     if (desc->num_workers < 0)
         return fail(GEMM_ERR_INVALID_VALUE, "num_workers must be >= 0");
     if ((desc->flags & ~(GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED |
-                         GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN | GEMM_FLAG_DEBUG_STAGE_FLAG_STALL)) != 0 ||
+                         GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN | GEMM_FLAG_DEBUG_STAGE_FLAG_STALL |
+                         GEMM_FLAG_CLAIM_AFTER_TILE)) != 0 ||
         (desc->flags & (GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED)) ==
             (GEMM_FLAG_STAGE_FLAGS_FUSED | GEMM_FLAG_STAGE_FLAGS_MERGED))
         return fail(GEMM_ERR_UNSUPPORTED, "unknown flags 0x%x (the two stage-flag layouts exclude each other)",
@@ -319,6 +321,7 @@ gemm_status build_core(const gemm_desc *desc, PlanCore &core)
     // device only, so every schedule and worker count sums in the same order.
     core.k_phase_row = tiles <= 4 * resident ? 2 : 0;
     core.full_excess = (desc->flags & GEMM_FLAG_DEBUG_STAGE_FLAG_STALL) != 0 ? 1 : 0;
+    core.claim_late = (desc->flags & GEMM_FLAG_CLAIM_AFTER_TILE) != 0 ? 1 : 0;
     return GEMM_OK;
 }
 
@@ -365,6 +368,7 @@ gemm_status fill_args(const PlanCore &core, const gemm_operands *ops, pts::GemmA
     args.round = core.round;
     args.full_excess = core.full_excess;
     args.k_phase_row = core.k_phase_row;
+    args.claim_late = core.claim_late;
     return GEMM_OK;
 }
 

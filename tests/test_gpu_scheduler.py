@@ -156,13 +156,13 @@ def test_probe_dynamic_xcd_late_worker_finds_nothing(pts):
     assert per_worker[3] == []
 
 
-def _traced_run(pts, shapes, schedule, tile=(0, 0), num_workers=0, out_dtype=torch.float32, k=64):
+def _traced_run(pts, shapes, schedule, tile=(0, 0), num_workers=0, out_dtype=torch.float32, k=64, flags=0):
     tensors = []
     for (m, n) in shapes:
         tensors.append((torch.zeros((max(m, 1), k), dtype=torch.bfloat16, device=U.DEV),
                         torch.zeros((max(n, 1), k), dtype=torch.bfloat16, device=U.DEV),
                         torch.empty((max(m, 1), max(n, 1)), dtype=out_dtype, device=U.DEV)))
-    with pts.Plan([(m, n, k) for (m, n) in shapes], out_dtype, tile, schedule, num_workers) as p:
+    with pts.Plan([(m, n, k) for (m, n) in shapes], out_dtype, tile, schedule, num_workers, flags) as p:
         buf = torch.zeros(p.trace_bytes() // 4 + 4, dtype=torch.int32, device=U.DEV)
         p.set_trace(buf)
         p.run(tensors)
@@ -337,3 +337,44 @@ def test_plans_created_and_destroyed_do_not_leak(pts):
     torch.cuda.synchronize()
     free1, _ = torch.cuda.mem_get_info()
     assert free1 >= free0 - (2 << 20), f"free memory fell by {free0 - free1} bytes over 500 plans"
+
+
+@pytest.mark.parametrize("schedule", ["dynamic", "dynamic_xcd"])
+def test_claim_after_tile_same_d_and_valid_claims(pts, schedule):
+    # Request-ahead off ("Advanced scheduling: Cluster Launch Control", section
+    # on overlapping the request with the current computation, as a baseline):
+    # the next tile is requested only after the epilogue. D must be bit-identical
+    # to the default (the summation order does not depend on who computes a
+    # tile), every tile computed once, the claims valid and the counters reset.
+    shapes = [(1000, 1500, 296), (600, 700, 1000), (257, 129, 64)]
+    ops = []
+    for g, (m, n, k) in enumerate(shapes):
+        a = gen.uniform_bf16_torch(m * k, 10 + g, 1, U.DEV).view(m, k)
+        b = gen.uniform_bf16_torch(n * k, 10 + g, 2, U.DEV).view(n, k)
+        ops.append((a, b))
+    outs = {}
+    for flags in (0, pts.GEMM_FLAG_CLAIM_AFTER_TILE):
+        U.log(f"claim after tile: {schedule} flags {flags}")
+        ds = [torch.full((m, n), float("nan"), dtype=torch.float32, device=U.DEV) for (m, n, _) in shapes]
+        with pts.Plan(shapes, torch.float32, (0, 0), schedule, 0, flags) as p:
+            buf = torch.zeros(p.trace_bytes() // 4 + 4, dtype=torch.int32, device=U.DEV)
+            p.set_trace(buf)
+            for _ in range(2):
+                p.run([(a, b, d) for (a, b), d in zip(ops, ds)])
+            torch.cuda.synchronize()
+            tiles, workers = pts.decode_trace(buf, p.num_tiles, p.num_workers)
+            nt, nw, counters = p.num_tiles, p.num_workers, p.counters()
+        assert sorted(tiles["tile"].tolist()) == list(range(nt))
+        order = np.lexsort((tiles["seq"], tiles["worker"]))
+        per_worker = [[] for _ in range(nw)]
+        for i in order:
+            per_worker[tiles["worker"][i]].append(int(tiles["claim"][i]))
+        if schedule == "dynamic":
+            oracle.check_dynamic_claims(per_worker, nt)
+        else:
+            check_xcd_claims(per_worker, (workers["xcc_id"] % 8).tolist(), nt, nw)
+        U.check_counters(schedule, counters, nt, nw)
+        outs[flags] = [d.cpu() for d in ds]
+    for d0, d1 in zip(outs[0], outs[pts.GEMM_FLAG_CLAIM_AFTER_TILE]):
+        assert not torch.isnan(d1).any()
+        assert torch.equal(d0.view(torch.int32), d1.view(torch.int32))
