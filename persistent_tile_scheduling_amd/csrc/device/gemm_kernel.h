@@ -379,10 +379,7 @@ struct Mainloop {
         full_tile = t.vm == C::BM && t.vn == C::BN;
         a_shift = (uint32_t)(4 * C::A_LOADS * C::ROWS_PER_LOAD * t.lda * 2);
         b_shift = (uint32_t)(4 * C::B_LOADS * C::ROWS_PER_LOAD * t.ldb * 2);
-        // Rows and chunks from an index the compiler cannot see through: the
-        // per-lane values would otherwise be hoisted out of the tile loop and,
-        // live across every k loop, go to scratch.
-        const int ln = (int)opaque_v((uint32_t)lane);
+        const int ln = lane;
         const int rl = ln / C::CHUNKS;
 #pragma unroll
         for (int i = 0; i < C::A_LOADS; ++i) {
@@ -1533,6 +1530,11 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
         const uint64_t t_tile0 = tracing ? realtime() : 0;
         const uint64_t c_tile0 = tracing ? shader_cycles() : 0;
         const TileCtx<C> tc = decode_tile<C>(args, cur.pos, group_begin);
+        // Every per-lane value of the k loop is formed per tile from a lane
+        // index the compiler cannot see through: hoisted out of the tile loop
+        // it would stay live across every k loop, where no register is spare,
+        // and go to scratch.
+        ml.lane = (int)opaque_v((uint32_t)lane);
 
         typename C::Acc acc[C::MI][C::NI];
 #pragma unroll
