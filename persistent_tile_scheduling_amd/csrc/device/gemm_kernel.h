@@ -726,8 +726,17 @@ struct Mainloop {
     // A[mi] is dead and its registers receive A[mi] of the next k-step; the B
     // fragments of the next k-step go to a second B set, read during the
     // first NI rows. One A set and two B sets are live.
+    // The last ROLL_SPARE rows of A have a second register set: odd k-steps
+    // use it, so the next k-step's fragments of those rows can be read early
+    // (after rows MI - 2 ROLL_SPARE ..) instead of after their own MFMAs, and
+    // a k-step's last read of its stage is issued ROLL_SPARE rows before the
+    // k-step ends. The stage barrier that follows k-step 0 waits for that read:
+    // one spare row (4 registers) took 2232 -> 2197 cycles per k-tile; two or
+    // three were no better or worse.
+    static constexpr int ROLL_SPARE = 1 < C::MI / 2 ? 1 : C::MI / 2;
     struct RollFrags {
         bf16x8 a[C::MI];
+        bf16x8 ax[ROLL_SPARE > 0 ? ROLL_SPARE : 1];
         bf16x8 b[2][C::NI];
     };
 
@@ -758,26 +767,38 @@ struct Mainloop {
                                                  int ks) const
     {
         static_assert(C::NI <= C::MI, "B reads ride on the first NI rows");
+        constexpr int SP = ROLL_SPARE, FIRST_EARLY = C::MI - 2 * SP;
+        static_assert(SP >= 0 && FIRST_EARLY >= 0, "spare rows");
         const uint8_t *sa = a_base(stage), *sb = b_base(stage);
 #pragma unroll
         for (int mi = 0; mi < C::MI; ++mi) {
+            const bool spare_row = mi >= C::MI - SP;
 #pragma unroll
             for (int ni = 0; ni < C::NI; ++ni)
-                acc[mi][ni] = C::Op::run(f.b[BS][ni], f.a[mi], acc[mi][ni]);
-            f.a[mi] = *(const bf16x8 *)(sa + frag_off[ks] + mi * C::MB * C::ROW_BYTES);
+                acc[mi][ni] = C::Op::run(f.b[BS][ni], (BS == 1 && spare_row) ? f.ax[mi - (C::MI - SP)] : f.a[mi],
+                                         acc[mi][ni]);
+            if (!spare_row)
+                f.a[mi] = *(const bf16x8 *)(sa + frag_off[ks] + mi * C::MB * C::ROW_BYTES);
             if (mi < C::NI)
                 f.b[BS ^ 1][mi] = *(const bf16x8 *)(sb + frag_off[ks] + mi * C::MB * C::ROW_BYTES);
+            if (mi >= FIRST_EARLY && mi < FIRST_EARLY + SP) {
+                // row r = MI - SP + j of the next k-step, into the set it will use
+                const int j = mi - FIRST_EARLY, r = C::MI - SP + j;
+                const bf16x8 v = *(const bf16x8 *)(sa + frag_off[ks] + r * C::MB * C::ROW_BYTES);
+                if (BS == 0)
+                    f.ax[j] = v;
+                else
+                    f.a[r] = v;
+            }
         }
-#pragma unroll
-        for (int mi = 0; mi < C::NI; ++mi) {
+        static_for<C::MI>([](auto row) {
+            constexpr int mi = decltype(row)::value;
+            constexpr int reads = (mi < C::MI - SP ? 1 : 0) + (mi < C::NI ? 1 : 0) +
+                                  (mi >= FIRST_EARLY && mi < FIRST_EARLY + SP ? 1 : 0);
             __builtin_amdgcn_sched_group_barrier(0x008, C::NI, 0); // the row's MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // its A and B reads
-        }
-#pragma unroll
-        for (int mi = C::NI; mi < C::MI; ++mi) {
-            __builtin_amdgcn_sched_group_barrier(0x008, C::NI, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+            if constexpr (reads > 0)
+                __builtin_amdgcn_sched_group_barrier(0x100, reads, 0); // its reads
+        });
     }
 
     // The loads and stage barriers of run_burst_rolling without its fragment
