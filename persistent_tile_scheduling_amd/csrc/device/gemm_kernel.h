@@ -805,13 +805,11 @@ struct Mainloop {
     // reads and MFMAs (same calls in the same order, so every wave meets the
     // same barriers).
     template <class Hook>
-    __device__ __forceinline__ void run_rolling_idle(const TileCtx<C> &t, Hook &on_last_stage)
+    __device__ __forceinline__ void run_rolling_idle(const TileCtx<C> &t, Hook &on_last_stage, int pre = -1)
     {
         const int nk = t.nk;
-        issue_any(0, 0, t.k, nk);
-        stage_ready(0, t);
-        if (1 < nk)
-            issue_any(1, 1, t.k, nk);
+        // an idle wave exists only in an edge tile (every wave loads LOADS per stage)
+        first_stages<false>(t, pre);
         if (nk == 1)
             on_last_stage();
         for (int kt = 0; kt + 1 < nk; ++kt) {
@@ -964,18 +962,54 @@ struct Mainloop {
         rolling_step<1>(f, acc, stage ^ 1, 0);
     }
 
+    // The first two stages of a tile: issued here, or (`pre` >= 0) issued
+    // already, during the previous tile's epilogue and ahead of its D stores.
+    // pre = the number of stores each thread issued after them when that is
+    // exactly STORES (the previous tile was a full tile), else 0: the wait for
+    // stage 0 then leaves stage 1's loads and those stores in flight.
+    static constexpr int STORES = C::BM * C::BN * 2 / 16 / C::THREADS; // 16-byte bf16 stores per thread
+    template <bool FULL>
+    __device__ __forceinline__ void first_stages(const TileCtx<C> &t, int pre)
+    {
+        const int nk = t.nk;
+        // this wave's loads of one stage: 2 LOADS for a loading wave of a
+        // paired full tile (none for its partner), LOADS otherwise
+        constexpr int STAGE_LOADS = (FULL && PAIRED) ? 2 * C::LOADS : C::LOADS;
+        if (pre < 0) {
+            issue_any(0, 0, t.k, nk);
+            wait_vmcnt<0>();
+        } else if (pre == STORES && nk > 1) {
+            wait_vmcnt<STAGE_LOADS + STORES>();
+        } else if (pre == STORES) {
+            wait_vmcnt<STORES>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        if (is_tail(0, t.k))
+            zero_k_tail(0, 0, t.k);
+        barrier_lds();
+        if (pre < 0 && 1 < nk)
+            issue_any(1, 1, t.k, nk);
+    }
+
+    // Both first stages of tile t, ahead of the previous tile's D stores.
+    __device__ __forceinline__ void issue_first_two(const TileCtx<C> &t)
+    {
+        if (t.nk > 0)
+            issue_any(0, 0, t.k, t.nk);
+        if (t.nk > 1)
+            issue_any(1, 1, t.k, t.nk);
+    }
+
     template <bool FULL, class Hook>
     __device__ __forceinline__ void run_straight_t(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI],
-                                                   Hook &on_last_stage)
+                                                   Hook &on_last_stage, int pre = -1)
     {
         static_assert(C::KSTEPS == 2 && C::STAGES == 2, "two k-steps per k-tile, two stages");
         const int nk = t.nk;
         // the loop iteration whose k-tile is the partial last one (phys = nk - 1), or -1
         const int tail_it = (t.k % C::BK) != 0 ? nk - 1 - kt0 : -1;
-        issue_any(0, 0, t.k, nk);
-        stage_ready(0, t);
-        if (1 < nk)
-            issue_any(1, 1, t.k, nk);
+        first_stages<FULL>(t, pre);
         if (nk == 1)
             on_last_stage();
         RollFrags f;
@@ -999,7 +1033,7 @@ struct Mainloop {
 
     template <class Hook>
     __device__ __forceinline__ void run_straight(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI],
-                                                 Hook &on_last_stage)
+                                                 Hook &on_last_stage, int pre = -1)
     {
         if (t.nk == 0) {
             on_last_stage();
@@ -1009,13 +1043,13 @@ struct Mainloop {
         // an edge tile computes nothing: it only loads and meets the stage
         // barriers.
         if (wm * C::WTM >= t.vm || wn * C::WTN >= t.vn) {
-            run_rolling_idle(t, on_last_stage);
+            run_rolling_idle(t, on_last_stage, pre);
             return;
         }
         if (full_tile)
-            run_straight_t<true>(t, acc, on_last_stage);
+            run_straight_t<true>(t, acc, on_last_stage, pre);
         else
-            run_straight_t<false>(t, acc, on_last_stage);
+            run_straight_t<false>(t, acc, on_last_stage, pre);
     }
 
     // ---- one wave per SIMD (16x16 blocks) ------------------------------------
@@ -1487,6 +1521,87 @@ __device__ __forceinline__ void store_epilogue_wide(const TileCtx<C> &t, const t
     }
 }
 
+// bf16 D of the 8-wave barrier kernels, staged per wave: each wave turns one
+// 16-row block of its wave tile at a time around in a private LDS area of its
+// own (beside the ring, so the next tile's first stages can load meanwhile)
+// and stores it as whole rows. Lane l of a 16x16 block holds 4 consecutive
+// columns 4(l/16) .. +3 of row l%16; converted to bf16 (round to nearest
+// even, the same as a store would) they go to the wave's area row-major, then
+// each lane reads 16-byte chunks back eight to a row, and one store writes
+// 8 rows x WTN * 2 contiguous bytes. No workgroup barrier is needed: only the
+// wave itself uses its area, and a wave's LDS operations are performed in
+// order. Only rows < M and columns < N are written (the element-wise path for
+// a chunk that crosses column N or a row that is not 16-byte aligned).
+template <class C>
+struct WaveEpilogue {
+    static constexpr int PITCH = C::WTN * 2 + 16;            // a staged row, padded
+    static constexpr int AREA = C::MB * PITCH;               // one wave's area
+    static constexpr int LDS_BYTES = C::WAVES * AREA;
+    static constexpr int CHUNKS_ROW = C::WTN * 2 / 16;       // 16-byte chunks per wave-tile row
+    static constexpr int ROWS = 64 / CHUNKS_ROW;             // rows per read (one chunk per lane)
+    static constexpr int READS = C::MB / ROWS;               // reads (and stores) per row block
+    static_assert(C::MB == 16 && C::OUT_BF16 && 64 % CHUNKS_ROW == 0 && C::MB % ROWS == 0, "wave-staged bf16 D");
+    static_assert(C::MI * READS == C::BM * C::BN * 2 / 16 / C::THREADS, "every thread stores the same count");
+};
+
+template <class C>
+__device__ __forceinline__ void store_epilogue_wave(const TileCtx<C> &t, const typename C::Acc (&acc)[C::MI][C::NI],
+                                                    int wm, int wn, int lane, int wave, uint8_t *area_base)
+{
+    using E = WaveEpilogue<C>;
+    lane = (int)opaque_v((uint32_t)lane);
+    uint8_t *const area = area_base + wave * E::AREA;
+    const int lr = lane % 16, lc = (lane / 16) * 4;
+    const int rr = lane / E::CHUNKS_ROW, cc = lane % E::CHUNKS_ROW; // this lane's chunk of a read
+    const int row = wm * C::WTM + rr, col = wn * C::WTN + cc * 8;     // in the tile
+    uint8_t *const base = (uint8_t *)t.d + ((int64_t)(t.row0 + row) * t.ldd + t.col0 + col) * 2;
+    const bool full = t.vec_ok && t.vm == C::BM && t.vn == C::BN;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < C::NI; ++ni) {
+            const typename C::Acc &v = acc[mi][ni];
+            bf16x4 h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                h[e] = (__bf16)v[e];
+            *(bf16x4 *)(area + lr * E::PITCH + (ni * 16 + lc) * 2) = h;
+        }
+        u32x4 chunk[E::READS];
+#pragma unroll
+        for (int j = 0; j < E::READS; ++j)
+            chunk[j] = *(const u32x4 *)(area + (j * E::ROWS + rr) * E::PITCH + cc * 16);
+#pragma unroll
+        for (int j = 0; j < E::READS; ++j) {
+            uint8_t *const dst = base + ((int64_t)(mi * C::MB + j * E::ROWS) * t.ldd) * 2;
+            if (full) {
+                __builtin_nontemporal_store(chunk[j], (u32x4 *)dst);
+            } else {
+                const int i = row + mi * C::MB + j * E::ROWS;
+                if (i < t.vm && col < t.vn) {
+                    if (t.vec_ok && col + 8 <= t.vn) {
+                        __builtin_nontemporal_store(chunk[j], (u32x4 *)dst);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (col + e < t.vn)
+                                ((uint16_t *)dst)[e] = (uint16_t)(chunk[j][e / 2] >> (16 * (e % 2)));
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <class C, bool USED>
+constexpr int wave_epilogue_lds_bytes()
+{
+    if constexpr (USED)
+        return WaveEpilogue<C>::LDS_BYTES;
+    else
+        return 0;
+}
+
 template <class C, bool WIDE>
 constexpr int epilogue_lds_bytes()
 {
@@ -1507,10 +1622,14 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     // settle the load here, so no wait for it lands inside the tile loop
     // (where it would also wait for the previous tile's stores)
     wait_vmcnt<0>();
-    // the two-waves-per-SIMD 16x16 kernels stage bf16 D as bf16 (WideEpilogue)
+    // the two-waves-per-SIMD 16x16 kernels stage bf16 D as bf16 (WideEpilogue);
+    // with the barrier hand-off they stage it per wave, beside the ring, and
+    // load the next tile's first stages during the epilogue (WaveEpilogue)
     constexpr bool WIDE_EPI = C::WAVES == 8 && C::MB == 16 && C::OUT_BF16;
-    constexpr int EPI_BYTES = epilogue_lds_bytes<C, WIDE_EPI>();
-    constexpr int SMEM_BYTES = C::LDS_BYTES > EPI_BYTES ? C::LDS_BYTES : EPI_BYTES;
+    constexpr bool PREFETCH = WIDE_EPI && C::SYNC == SYNC_BARRIER;
+    constexpr int EPI_BYTES = PREFETCH ? 0 : epilogue_lds_bytes<C, WIDE_EPI>();
+    constexpr int WAVE_EPI_BYTES = wave_epilogue_lds_bytes<C, PREFETCH>();
+    constexpr int SMEM_BYTES = (C::LDS_BYTES > EPI_BYTES ? C::LDS_BYTES : EPI_BYTES) + WAVE_EPI_BYTES;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
     __shared__ int32_t sched_slots[4];
     __shared__ uint32_t stage_flags[6];
@@ -1547,7 +1666,73 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     const bool claim_late = args->claim_late != 0;
     Claimed cur = sched.first(tid);
     int seq = 0;
-    while (cur.pos < total_tiles) {
+    if constexpr (PREFETCH) {
+        // Tile i's epilogue overlaps tile i + 1's first loads: once the k loop
+        // is done (every wave past its last read of the ring: the barrier
+        // below, which also publishes the next claim) the next tile is decoded
+        // and both of its first stages are loaded while this tile's D is
+        // staged per wave and stored; the next tile then waits for its stage 0
+        // only, with this tile's stores still in flight.
+        TileCtx<C> tc{};
+        if (cur.pos < total_tiles) {
+            tc = decode_tile<C>(args, cur.pos, group_begin);
+            ml.lane = (int)opaque_v((uint32_t)lane);
+            ml.setup(tc);
+        }
+        int pre = -1;
+        while (cur.pos < total_tiles) {
+            const uint64_t t_tile0 = tracing ? realtime() : 0;
+            const uint64_t c_tile0 = tracing ? shader_cycles() : 0;
+            typename C::Acc acc[C::MI][C::NI];
+#pragma unroll
+            for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < C::NI; ++ni)
+                    acc[mi][ni] = typename C::Acc{};
+            auto claim = [&] {
+                if (!claim_late)
+                    sched.claim_ahead(leader);
+            };
+            ml.run_straight(tc, acc, claim, pre);
+            if (claim_late)
+                sched.claim_ahead(leader);
+            sched.stage_next(tid, seq);
+            barrier_lds();
+            const Claimed next = sched.read_next(cur, seq);
+            TileCtx<C> tn{};
+            if (next.pos < total_tiles) {
+                tn = decode_tile<C>(args, next.pos, group_begin);
+                ml.lane = (int)opaque_v((uint32_t)lane);
+                ml.setup(tn);
+                ml.issue_first_two(tn);
+            }
+            store_epilogue_wave<C>(tc, acc, ml.wm, ml.wn, lane, wave, smem + C::LDS_BYTES);
+            pre = (tc.vec_ok && tc.vm == C::BM && tc.vn == C::BN) ? Mainloop<C>::STORES : 0;
+            if (tracing && leader) {
+                TileTrace r;
+                r.tile = cur.pos;
+                r.claim = cur.claim;
+                r.worker = blockIdx.x;
+                r.seq = seq;
+                r.group = tc.problem;
+                r.row0 = tc.row0;
+                r.col0 = tc.col0;
+                r.xcc_id = xcc_id_reg();
+                r.t_start = t_tile0;
+                r.t_end = realtime();
+                r.cycles = (uint32_t)(shader_cycles() - c_tile0);
+                r.pad = 0;
+                ((TileTrace *)trace)[cur.pos] = r;
+                // (the record's stores are younger still: the next tile's
+                // stage-0 wait then waits for a little more, never for less)
+            }
+            tc = tn;
+            cur = next;
+            ++seq;
+        }
+        wait_vmcnt<0>();
+    }
+    while (!PREFETCH && cur.pos < total_tiles) {
         const uint64_t t_tile0 = tracing ? realtime() : 0;
         const uint64_t c_tile0 = tracing ? shader_cycles() : 0;
         const TileCtx<C> tc = decode_tile<C>(args, cur.pos, group_begin);
