@@ -140,13 +140,14 @@ typedef struct {
 /*
  * Claim timing of the dynamic schedules (request-ahead off). By default a
  * worker asks for its next tile once the current tile's last stage is in LDS,
- * so the request's round trip overlaps the last k-tile and the epilogue (the
- * Cluster Launch Control page, section on overlapping the request with the
- * current computation). With this flag the request goes out only after the
- * tile's epilogue and the worker waits for the answer before it starts the
- * next tile: the baseline that shows what the overlap is worth. Results are
- * identical; the static and non-persistent schedules issue no requests and
- * ignore it.
+ * so the request's round trip overlaps the last k-tile (the Cluster Launch
+ * Control page, section on overlapping the request with the current
+ * computation). With this flag the request goes out only once the tile's
+ * computation is done (after its k loop in the default 256x256 kernel with
+ * bf16 output, which starts the next tile's loads before its epilogue; after
+ * its epilogue in the other kernels) and the worker waits for the answer: the
+ * baseline that shows what the overlap is worth. Results are identical; the
+ * static and non-persistent schedules issue no requests and ignore it.
  */
 #define GEMM_FLAG_CLAIM_AFTER_TILE 16u
 
