@@ -434,6 +434,61 @@ def tile_cycle_fit(pts, schedule="static", ks=(1024, 2048, 4096, 8192), mn=8192)
                 mfma_ideal_cycles_per_k_tile=2048)
 
 
+def mfma_ceiling(pts, steps, warmup, isolated=15, ksteps=1024):
+    """The matrix-unit ceiling probe (the default kernel's MFMA work with no
+    memory traffic, one workgroup of 8 waves per compute unit; ksteps = 1024
+    is the FLOP of one 8192^3 GEMM): `steps` launches back to back after
+    `warmup`, as the headline times the GEMM, then `isolated` single launches
+    with idle time between them. Operand fragments are drawn like A and B."""
+    import numpy as np
+    import pts_inputs as gen
+    import torch
+    frags = gen.uniform_bf16_torch(pts.PTS_MFMA_CEILING_FRAG_BYTES // 2, 0, gen.TENSOR_A, "cuda")
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    stamps = torch.zeros(blocks * 2, dtype=torch.int64, device="cuda")
+    flops = blocks * 8 * ksteps * 32 * 16384.0
+    stream = torch.cuda.Stream()
+
+    def clock_ghz():
+        st = stamps.view(-1, 2).cpu().numpy().astype(np.float64)
+        return float(np.median(st[:, 0] / (st[:, 1] * 10.0)))
+
+    for _ in range(warmup):
+        pts.pts_mfma_ceiling(frags, out, stamps, blocks, ksteps, stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        pts.pts_mfma_ceiling(frags, out, stamps, blocks, ksteps, stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    kms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    back_clock = clock_ghz()
+    iso, iso_clock = [], []
+    for _ in range(isolated):
+        time.sleep(0.05)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pts.pts_mfma_ceiling(frags, out, stamps, blocks, ksteps, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        iso.append(e0.elapsed_time(e1))
+        iso_clock.append(clock_ghz())
+    avg = sum(kms) / len(kms)
+    med_iso = sorted(iso)[len(iso) // 2]
+    return dict(blocks=blocks, waves_per_block=8, k_steps=ksteps, flop_per_launch=flops,
+                back_to_back=dict(launches=steps, kernel_ms_avg=round(avg, 5),
+                                  tflops=round(flops / (avg * 1e-3) / 1e12, 1),
+                                  frac=round(flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                  clock_ghz_last_launch=round(back_clock, 3)),
+                isolated=dict(launches=isolated, kernel_ms_median=round(med_iso, 5),
+                              tflops=round(flops / (med_iso * 1e-3) / 1e12, 1),
+                              frac=round(flops / (med_iso * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                              clock_ghz_median=round(float(np.median(iso_clock)), 3)))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -468,6 +523,8 @@ def main():
                     help="interleaved rounds per schedule on each imbalanced workload")
     ap.add_argument("--tile-cycles", action="store_true",
                     help="only fit shader cycles per tile against K (8192 x 8192 x K, K = 1024..8192) and print it")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only time the matrix-unit ceiling probe (the GEMM's MFMA work without memory traffic)")
     ap.add_argument("--calibration-copy", type=int, default=0,
                     help="also run one int16 copy of this many elements (PMC calibration)")
     args = ap.parse_args()
@@ -486,6 +543,13 @@ def main():
     if args.tile_cycles:
         fit = tile_cycle_fit(pts)
         print(json.dumps({"tile_cycle_fit": fit}), flush=True)
+        return
+    if args.mfma_ceiling:
+        ceil = mfma_ceiling(pts, args.steps, args.warmup)
+        print(f"# MFMA ceiling: back to back {ceil['back_to_back']['tflops']} TFLOP/s "
+              f"(frac {ceil['back_to_back']['frac']}), isolated {ceil['isolated']['tflops']} TFLOP/s",
+              file=sys.stderr, flush=True)
+        print(json.dumps({"mfma_ceiling": ceil}), flush=True)
         return
     wl = workload(args.workload)
     wl["tile"] = tuple(wl["tile"][:2]) + (args.tile_k, args.stages, args.load_path, args.waves, args.mfma)

@@ -391,6 +391,27 @@ gemm_status pts_sched_probe(int32_t num_tiles, int32_t num_workers, int32_t sche
                             int32_t *out_tiles, int32_t *out_counts, int32_t max_per_worker,
                             uint32_t *counters, uint32_t *out_status, void *stream);
 
+/*
+ * Matrix-unit ceiling probe: the default GEMM kernel's MFMA work (8 waves per
+ * workgroup, each running the 32 v_mfma_f32_16x16x32_bf16 of one k-step of a
+ * 128x64 accumulator block per step) with no memory traffic inside its loop,
+ * for measuring what the matrix units sustain under the power limit beside
+ * the GEMM ("Pipeline Groups", section "Overview": the MMA consumer alone,
+ * with its loaders and store taken away). One launch does
+ * blocks x 8 x steps x 32 x 16384 FLOP; num_blocks = 0 runs one workgroup per
+ * compute unit, and steps = 1024 then matches the FLOP of one 8192^3 GEMM.
+ * frags: device array of PTS_MFMA_CEILING_FRAG_BYTES bytes (bf16 operand
+ * fragments, read once), 16-byte aligned. out: device array of
+ * num_blocks x 512 floats (per thread, the sum of its accumulators: with every
+ * fragment element 1.0 each is 4096 x steps). stamps: device array of
+ * num_blocks x 2 uint64 (shader cycles, then 100 MHz ticks, of each
+ * workgroup's loop). steps must be even and >= 2, num_blocks in [0, 65536];
+ * GEMM_ERR_INVALID_VALUE otherwise, with nothing launched.
+ */
+#define PTS_MFMA_CEILING_FRAG_BYTES 196608
+gemm_status pts_mfma_ceiling(const void *frags, float *out, uint64_t *stamps, int32_t num_blocks, int32_t steps,
+                             void *stream);
+
 #ifdef __cplusplus
 }
 #endif

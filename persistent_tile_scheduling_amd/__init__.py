@@ -43,6 +43,7 @@ GEMM_FLAG_STAGE_FLAGS_MERGED = 2
 GEMM_FLAG_PROBLEM_ORDER_AS_GIVEN = 4
 GEMM_FLAG_DEBUG_STAGE_FLAG_STALL = 8
 GEMM_FLAG_CLAIM_AFTER_TILE = 16
+PTS_MFMA_CEILING_FRAG_BYTES = 196608
 
 TILE_TRACE_BYTES = 56
 WORKER_TRACE_BYTES = 32
@@ -97,6 +98,7 @@ def _load():
         "pts_stream_destroy": (ctypes.c_int, [P]),
         "pts_sched_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int64, ctypes.c_int64, P, P, ctypes.c_int32, P, P, P]),
+        "pts_mfma_ceiling": (ctypes.c_int, [P, P, P, ctypes.c_int32, ctypes.c_int32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -242,6 +244,12 @@ def pts_sched_probe(num_tiles: int, num_workers: int, schedule: int, gate_worker
                                 ctypes.c_void_p(_ptr(out_tiles)), ctypes.c_void_p(_ptr(out_counts)),
                                 max_per_worker, ctypes.c_void_p(_ptr(counters)),
                                 ctypes.c_void_p(_ptr(out_status)), ctypes.c_void_p(_stream_handle(stream))))
+
+
+def pts_mfma_ceiling(frags, out, stamps, num_blocks: int, steps: int, stream=None) -> None:
+    _check(_lib.pts_mfma_ceiling(ctypes.c_void_p(_ptr(frags)), ctypes.c_void_p(_ptr(out)),
+                                 ctypes.c_void_p(_ptr(stamps)), num_blocks, steps,
+                                 ctypes.c_void_p(_stream_handle(stream))))
 
 
 # ---------------------------------------------------------------------------

@@ -1,4 +1,5 @@
-// Auxiliary kernels: the grid-stride int16 copy and the scheduler probe.
+// Auxiliary kernels: the grid-stride int16 copy, the scheduler probe and the
+// matrix-unit ceiling probe.
 #pragma once
 
 #include "common.h"
@@ -82,6 +83,66 @@ __global__ __launch_bounds__(64) void sched_probe_kernel(int32_t num_tiles, int3
     if (leader && gate_worker >= 0 && w != gate_worker)
         __hip_atomic_fetch_add(counters + CTR_GATE, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     sched.finish(leader);
+}
+
+// Matrix-unit ceiling probe: the default GEMM kernel's matrix work without
+// its memory traffic. A workgroup is 8 waves (two per SIMD, as in the GEMM);
+// each wave keeps a 128x64 block of fp32 accumulators (8 x 4 blocks of 16x16)
+// and per step runs the 32 v_mfma_f32_16x16x32_bf16 of one k-step. Its 24
+// operand fragments (two k-steps' worth of 8 A rows and 4 B columns) are read
+// once from `frags` and alternate by step parity, so operand values change
+// from one MFMA to the next as in the GEMM's k loop. Inside the loop there are
+// no loads, LDS accesses or stores: the rate it reaches is the matrix units'
+// rate under the chip's power limit with operands of the same values.
+//
+// frags: 8 waves x 24 fragments x 64 lanes x 16 bytes (8 bf16), fragment f of
+// wave w at [(w * 24 + f) * 64 + lane]. out[block * 512 + thread]: the sum of
+// that thread's 128 accumulators. stamps[block * 2 + {0, 1}]: shader-clock
+// cycles and 100 MHz real-time ticks from the loop's start to its end, taken
+// by the first wave.
+__global__ __launch_bounds__(512) void mfma_ceiling_kernel(const bf16x8 *__restrict__ frags, float *__restrict__ out,
+                                                           uint64_t *__restrict__ stamps, int32_t steps)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    bf16x8 a[2][8], b[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            a[h][i] = frags[(wave * 24 + h * 12 + i) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            b[h][j] = frags[(wave * 24 + h * 12 + 8 + j) * 64 + lane];
+    }
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    wait_all();
+    const uint64_t c0 = shader_cycles(), t0 = realtime();
+    for (int s = 0; s < steps; s += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[h][j], a[h][i], acc[i][j], 0, 0, 0);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            sum += (acc[i][j][0] + acc[i][j][1]) + (acc[i][j][2] + acc[i][j][3]);
+    const uint64_t c1 = shader_cycles(), t1 = realtime();
+    out[(int64_t)blockIdx.x * 512 + threadIdx.x] = sum;
+    if (threadIdx.x == 0) {
+        stamps[2 * (int64_t)blockIdx.x] = c1 - c0;
+        stamps[2 * (int64_t)blockIdx.x + 1] = t1 - t0;
+    }
 }
 
 } // namespace pts

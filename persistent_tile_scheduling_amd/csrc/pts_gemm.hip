@@ -752,4 +752,31 @@ gemm_status pts_sched_probe(int32_t num_tiles, int32_t num_workers, int32_t sche
     return e == hipSuccess ? GEMM_OK : hip_fail(e, "probe launch");
 }
 
+gemm_status pts_mfma_ceiling(const void *frags, float *out, uint64_t *stamps, int32_t num_blocks, int32_t steps,
+                             void *stream)
+{
+    if (steps < 2 || (steps & 1) != 0)
+        return fail(GEMM_ERR_INVALID_VALUE, "steps must be even and >= 2");
+    if (num_blocks < 0 || num_blocks > 65536)
+        return fail(GEMM_ERR_INVALID_VALUE, "num_blocks must be in [0, 65536]");
+    if (frags == nullptr || out == nullptr || stamps == nullptr)
+        return fail(GEMM_ERR_INVALID_VALUE, "NULL pointer");
+    if (((uintptr_t)frags % 16) != 0 || ((uintptr_t)out % 4) != 0 || ((uintptr_t)stamps % 8) != 0)
+        return fail(GEMM_ERR_INVALID_VALUE, "frags must be 16-byte, out 4-byte, stamps 8-byte aligned");
+    int blocks = num_blocks;
+    if (blocks == 0) {
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess)
+            return hip_fail(e, "device query");
+        blocks = cus;
+    }
+    hipLaunchKernelGGL(pts::mfma_ceiling_kernel, dim3(blocks), dim3(512), 0, (hipStream_t)stream,
+                       (const pts::bf16x8 *)frags, out, stamps, steps);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? GEMM_OK : hip_fail(e, "ceiling probe launch");
+}
+
 } // extern "C"

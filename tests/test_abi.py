@@ -112,6 +112,11 @@ def test_null_arguments(binding):
     assert lib.pts_copy_int16(None, None, 0, 0, None) == binding.GEMM_OK     # empty copy is a no-op
     assert lib.pts_sched_probe(12, 0, 0, -1, 0, 0, None, None, 1, None, None, None) == 1
     assert lib.pts_stream_create_cu_masked(4, None) == binding.GEMM_ERR_INVALID_VALUE
+    # the ceiling probe checks its sizes and pointers before any launch
+    assert lib.pts_mfma_ceiling(None, None, None, 1, 2, None) == binding.GEMM_ERR_INVALID_VALUE
+    assert lib.pts_mfma_ceiling(16, 16, 16, 1, 3, None) == binding.GEMM_ERR_INVALID_VALUE     # odd steps
+    assert lib.pts_mfma_ceiling(16, 16, 16, -1, 2, None) == binding.GEMM_ERR_INVALID_VALUE
+    assert lib.pts_mfma_ceiling(24, 16, 16, 1, 2, None) == binding.GEMM_ERR_INVALID_VALUE     # misaligned
     assert lib.pts_stream_destroy(None) == binding.GEMM_OK
     assert "NULL" in binding.gemm_last_error() or binding.gemm_last_error() != ""
 
@@ -130,7 +135,7 @@ def test_product_path_does_not_touch_the_oracle():
 def test_header_constants_match_the_binding(binding):
     import re
     text = open(os.path.join(ROOT, "include", "pts_gemm.h")).read()
-    defines = dict(re.findall(r"#define (GEMM_[A-Z_]+) (\d+)", text))
+    defines = dict(re.findall(r"#define ((?:GEMM|PTS)_[A-Z_]+) (\d+)", text))
     assert defines, "no numeric constants found in the header"
     for name, value in defines.items():
         assert getattr(binding, name) == int(value), name
