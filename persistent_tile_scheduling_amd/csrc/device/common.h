@@ -193,6 +193,16 @@ __device__ __forceinline__ uint32_t opaque_v(uint32_t v)
     return v;
 }
 
+// This lane's index in the wave (0..63), computed afresh from the exec mask
+// (which must be all ones): nothing holds it in a register between uses, and
+// the compiler cannot merge two computations of it into one long-lived value.
+__device__ __forceinline__ uint32_t lane_id()
+{
+    uint32_t v;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+    return v;
+}
+
 __device__ __forceinline__ int uniform(int v)
 {
     return __builtin_amdgcn_readfirstlane(v);

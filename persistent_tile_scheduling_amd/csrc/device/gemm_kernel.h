@@ -706,14 +706,20 @@ struct Mainloop {
     // k-tile's stage is ready and no further load of this tile is waited for
     // with vmcnt, so a memory operation it issues overlaps the last k-tile's
     // MFMAs and the epilogue without any load wait stalling on it.
+    //
+    // `pre` >= 0: the tile's first two stages were issued before this call
+    // (during the previous tile's epilogue), followed by `pre` stores of
+    // this thread (the first stage wait leaves both in flight); -1: nothing
+    // was issued yet. Only the 16x16 barrier-hand-off loops take it.
     template <class Hook>
-    __device__ __forceinline__ void run(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI], Hook &&on_last_stage)
+    __device__ __forceinline__ void run(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI], Hook &&on_last_stage,
+                                        int pre = -1)
     {
         static_assert(C::STAGES == 2 && C::LOAD_PATH == LOAD_DMA, "the built k loops use a two-stage ring");
         if constexpr (C::MB == 16 && C::WAVES == 4)
-            run_single(t, acc, on_last_stage);
+            run_single(t, acc, on_last_stage, pre);
         else if constexpr (C::MB == 16 && C::SYNC == SYNC_BARRIER)
-            run_straight(t, acc, on_last_stage);
+            run_straight(t, acc, on_last_stage, pre);
         else if constexpr (C::MB == 16)
             run_burst_rolling(t, acc, on_last_stage);
         else
@@ -1147,7 +1153,7 @@ struct Mainloop {
     // order, so the result does not depend on which form ran.
     template <class Hook>
     __device__ __forceinline__ void run_single(const TileCtx<C> &t, typename C::Acc (&acc)[C::MI][C::NI],
-                                               Hook &on_last_stage)
+                                               Hook &on_last_stage, int pre = -1)
     {
         static_assert(C::STAGES == 2 && C::KSTEPS == 2 && C::LOAD_PATH == LOAD_DMA && !PAIRED, "one-wave layout");
         const int nk = t.nk;
@@ -1155,10 +1161,7 @@ struct Mainloop {
             on_last_stage();
             return; // the accumulators keep their zeros
         }
-        issue_any(0, 0, t.k, nk);
-        stage_ready(0, t);
-        if (1 < nk)
-            issue_any(1, 1, t.k, nk);
+        first_stages<false>(t, pre);
         if (nk == 1)
             on_last_stage();
         Frags f0, f1;
@@ -1623,10 +1626,12 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     // (where it would also wait for the previous tile's stores)
     wait_vmcnt<0>();
     // the two-waves-per-SIMD 16x16 kernels stage bf16 D as bf16 (WideEpilogue);
-    // with the barrier hand-off they stage it per wave, beside the ring, and
-    // load the next tile's first stages during the epilogue (WaveEpilogue)
+    // with the barrier hand-off they, and the one-wave-per-SIMD 16x16 kernel,
+    // stage it per wave, beside the ring, and load the next tile's first
+    // stages during the epilogue (WaveEpilogue)
     constexpr bool WIDE_EPI = C::WAVES == 8 && C::MB == 16 && C::OUT_BF16;
-    constexpr bool PREFETCH = WIDE_EPI && C::SYNC == SYNC_BARRIER;
+    constexpr bool SINGLE_EPI = C::WAVES == 4 && C::MB == 16 && C::OUT_BF16;
+    constexpr bool PREFETCH = (WIDE_EPI || SINGLE_EPI) && C::SYNC == SYNC_BARRIER;
     constexpr int EPI_BYTES = PREFETCH ? 0 : epilogue_lds_bytes<C, WIDE_EPI>();
     constexpr int WAVE_EPI_BYTES = wave_epilogue_lds_bytes<C, PREFETCH>();
     constexpr int SMEM_BYTES = (C::LDS_BYTES > EPI_BYTES ? C::LDS_BYTES : EPI_BYTES) + WAVE_EPI_BYTES;
@@ -1673,10 +1678,13 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
         // and both of its first stages are loaded while this tile's D is
         // staged per wave and stored; the next tile then waits for its stage 0
         // only, with this tile's stores still in flight.
+        // (the lane index is recomputed where needed: kept live across the k
+        // loop it is spilled where no register is spare, and its reload's
+        // wait would also wait for the next tile's loads)
         TileCtx<C> tc{};
         if (cur.pos < total_tiles) {
             tc = decode_tile<C>(args, cur.pos, group_begin);
-            ml.lane = (int)opaque_v((uint32_t)lane);
+            ml.lane = (int)lane_id();
             ml.setup(tc);
         }
         int pre = -1;
@@ -1693,7 +1701,7 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
                 if (!claim_late)
                     sched.claim_ahead(leader);
             };
-            ml.run_straight(tc, acc, claim, pre);
+            ml.run(tc, acc, claim, pre);
             if (claim_late)
                 sched.claim_ahead(leader);
             sched.stage_next(tid, seq);
@@ -1702,11 +1710,11 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
             TileCtx<C> tn{};
             if (next.pos < total_tiles) {
                 tn = decode_tile<C>(args, next.pos, group_begin);
-                ml.lane = (int)opaque_v((uint32_t)lane);
+                ml.lane = (int)lane_id();
                 ml.setup(tn);
                 ml.issue_first_two(tn);
             }
-            store_epilogue_wave<C>(tc, acc, ml.wm, ml.wn, lane, wave, smem + C::LDS_BYTES);
+            store_epilogue_wave<C>(tc, acc, ml.wm, ml.wn, (int)lane_id(), wave, smem + C::LDS_BYTES);
             pre = (tc.vec_ok && tc.vm == C::BM && tc.vn == C::BN) ? Mainloop<C>::STORES : 0;
             if (tracing && leader) {
                 TileTrace r;
