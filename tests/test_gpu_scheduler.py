@@ -339,13 +339,18 @@ def test_plans_created_and_destroyed_do_not_leak(pts):
     assert free1 >= free0 - (2 << 20), f"free memory fell by {free0 - free1} bytes over 500 plans"
 
 
+@pytest.mark.parametrize("kernel", [(0, 0), (256, 256, 64, 2, 1, 4, 16)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("schedule", ["dynamic", "dynamic_xcd"])
-def test_claim_after_tile_same_d_and_valid_claims(pts, schedule):
+def test_claim_after_tile_same_d_and_valid_claims(pts, schedule, out_dtype, kernel):
     # Request-ahead off ("Advanced scheduling: Cluster Launch Control", section
     # on overlapping the request with the current computation, as a baseline):
     # the next tile is requested only after the epilogue. D must be bit-identical
     # to the default (the summation order does not depend on who computes a
     # tile), every tile computed once, the claims valid and the counters reset.
+    # bf16 output runs the tile loop that loads the next tile during the
+    # epilogue (both 256x256 kernels), fp32 output the staged one; the trace is
+    # on in every run.
     shapes = [(1000, 1500, 296), (600, 700, 1000), (257, 129, 64)]
     ops = []
     for g, (m, n, k) in enumerate(shapes):
@@ -354,9 +359,9 @@ def test_claim_after_tile_same_d_and_valid_claims(pts, schedule):
         ops.append((a, b))
     outs = {}
     for flags in (0, pts.GEMM_FLAG_CLAIM_AFTER_TILE):
-        U.log(f"claim after tile: {schedule} flags {flags}")
-        ds = [torch.full((m, n), float("nan"), dtype=torch.float32, device=U.DEV) for (m, n, _) in shapes]
-        with pts.Plan(shapes, torch.float32, (0, 0), schedule, 0, flags) as p:
+        U.log(f"claim after tile: {schedule} {out_dtype} kernel {kernel} flags {flags}")
+        ds = [torch.full((m, n), float("nan"), dtype=out_dtype, device=U.DEV) for (m, n, _) in shapes]
+        with pts.Plan(shapes, out_dtype, kernel, schedule, 0, flags) as p:
             buf = torch.zeros(p.trace_bytes() // 4 + 4, dtype=torch.int32, device=U.DEV)
             p.set_trace(buf)
             for _ in range(2):
@@ -377,4 +382,5 @@ def test_claim_after_tile_same_d_and_valid_claims(pts, schedule):
         outs[flags] = [d.cpu() for d in ds]
     for d0, d1 in zip(outs[0], outs[pts.GEMM_FLAG_CLAIM_AFTER_TILE]):
         assert not torch.isnan(d1).any()
-        assert torch.equal(d0.view(torch.int32), d1.view(torch.int32))
+        bits = torch.int32 if out_dtype == torch.float32 else torch.int16
+        assert torch.equal(d0.view(bits), d1.view(bits))
