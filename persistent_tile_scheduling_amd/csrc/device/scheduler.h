@@ -19,11 +19,12 @@
 //     several issuers would each take a coordinate);
 //   * the request for the next tile is issued while the current tile is being
 //     computed -- once its last ring stage is in LDS -- and its result is read
-//     only while the tile's accumulators are staged, so the atomic's round
-//     trip hides behind the last k-tile and the epilogue (section
-//     "Overlapping the request with the current computation"; issued at the
-//     tile's first k-tile instead, the round trip held up that tile's load
-//     waits, since vmcnt counts in issue order);
+//     only when the tile's k loop is done (the kernels that load the next
+//     tile during the epilogue) or while the accumulators are staged (the
+//     others), so the atomic's round trip hides behind the last k-tile
+//     (section "Overlapping the request with the current computation"; issued
+//     at the tile's first k-tile instead, the round trip held up that tile's
+//     load waits, since vmcnt counts in issue order);
 //   * the result reaches the other waves through an LDS slot and a barrier,
 //     as the CLC response reaches the CTA through shared memory;
 //   * a claim returning an index >= T is the failed request: the worker
