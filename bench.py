@@ -523,6 +523,8 @@ def main():
                     help="interleaved rounds per schedule on each imbalanced workload")
     ap.add_argument("--tile-cycles", action="store_true",
                     help="only fit shader cycles per tile against K (8192 x 8192 x K, K = 1024..8192) and print it")
+    ap.add_argument("--no-ceiling", dest="ceiling", action="store_false",
+                    help="leave the matrix-unit ceiling probe out of the default 8192^3 line")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only time the matrix-unit ceiling probe (the GEMM's MFMA work without memory traffic)")
     ap.add_argument("--calibration-copy", type=int, default=0,
@@ -609,6 +611,12 @@ def main():
     vendor = vendor_gemm(wl, ops, args.steps) if args.vendor and len(wl["shapes"]) == 1 else None
     if vendor:
         print(f"# vendor {vendor['library']}: {vendor['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    ceiling = None
+    if args.ceiling and args.workload == "c2":
+        # the same launch count back to back, the GEMM's MFMA work alone
+        ceiling = mfma_ceiling(pts, args.steps, args.warmup)
+        print(f"# MFMA ceiling: back to back {ceiling['back_to_back']['tflops']} TFLOP/s", file=sys.stderr,
+              flush=True)
 
     line = {
         "metric": METRIC,
@@ -646,6 +654,11 @@ def main():
         line["roofline"]["frac_at_measured_clock"] = round(head["kernel_tflops"] / peak_at_clock, 4)
     if vendor:
         line["vendor_library"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in vendor.items()}
+    if ceiling:
+        b2b = ceiling["back_to_back"]
+        line["mfma_ceiling"] = {"kernel": "pts::mfma_ceiling_kernel", "tflops": b2b["tflops"], "frac": b2b["frac"],
+                                "clock_ghz": b2b["clock_ghz_last_launch"],
+                                "gemm_over_ceiling": round(head["kernel_tflops"] / b2b["tflops"], 4)}
     if "static" in results and "kernel_ms_median" in results["static"]:
         line["dynamic_vs_static"] = {s: round(results["static"]["kernel_ms_median"] / r["kernel_ms_median"], 4)
                                      for s, r in results.items() if s != "static" and "kernel_ms_median" in r}
