@@ -173,15 +173,26 @@ struct GemmConfig {
 
 // LDS layout of one operand tile in a stage: row r (a row of A or a column of
 // B) holds its BK k-values in CHUNKS 16-byte chunks; logical chunk c sits at
-// physical position c ^ swz(r). The XOR spreads the 16-byte fragment reads of
-// one MFMA operand (16 consecutive rows, one chunk each) over distinct bank
-// groups whether the LDS serves 8 or 16 lanes per cycle. swz depends on
-// r mod 16 only, so a lane's fragment offsets repeat every 16 rows and the
-// per-block differences become instruction immediates.
-template <int BK>
+// physical position c ^ swz(r), chosen so that one wave-wide 16-byte-per-lane
+// fragment read takes the LDS's full width, measured with the LDS bank
+// conflict counter (a read of 64 consecutive 16-byte chunks is active 4
+// cycles and conflict-free; the same amount read in a conflicting pattern
+// takes 8).
+//   16x16x32 operands (MB = 16): lane l reads row l % 16, chunk 4 ks + l / 16.
+//     swz = (r >> 1) & 7 measures conflict-free; r ^ (r >> 3 & 1), which
+//     spreads any 16 consecutive lanes over distinct bank groups, measures
+//     4 conflict cycles per read.
+//   32x32x16 operands (MB = 32): lane l reads row l % 32, chunk l / 32 (+2 ks).
+//     r ^ (r >> 3 & 1) measures conflict-free; (r >> 2) & 7 does not.
+// swz depends on r mod 16 (mod 32 for MB = 32) only, so a lane's fragment
+// offsets repeat every MB rows and the per-block differences become
+// instruction immediates.
+template <int BK, int MB>
 __device__ __forceinline__ int lds_swizzle(int r)
 {
-    if constexpr (BK == 64)
+    if constexpr (BK == 64 && MB == 16)
+        return (r >> 1) & 7;
+    else if constexpr (BK == 64)
         return (r ^ ((r >> 3) & 1)) & 7;
     else
         return ((r >> 1) ^ ((r >> 3) & 1)) & 3;
@@ -190,7 +201,7 @@ __device__ __forceinline__ int lds_swizzle(int r)
 template <class C>
 __device__ __forceinline__ int lds_offset(int r, int c)
 {
-    return r * C::ROW_BYTES + ((c ^ lds_swizzle<C::BK>(r)) << 4);
+    return r * C::ROW_BYTES + ((c ^ lds_swizzle<C::BK, C::MB>(r)) << 4);
 }
 
 // Wait until this wave's loads of the oldest in-flight stage have landed,
@@ -343,7 +354,7 @@ struct Mainloop {
     __device__ __forceinline__ int load_chunk(int i, int nloads, int ln) const
     {
         const int r = (wave * nloads + i) * C::ROWS_PER_LOAD + ln / C::CHUNKS;
-        return (ln % C::CHUNKS) ^ lds_swizzle<C::BK>(r);
+        return (ln % C::CHUNKS) ^ lds_swizzle<C::BK, C::MB>(r);
     }
     __device__ __forceinline__ int load_chunk(int i, int nloads) const { return load_chunk(i, nloads, lane); }
 
@@ -536,7 +547,7 @@ struct Mainloop {
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks)
             frag_off[ks] =
-                (uint32_t)(lr * C::ROW_BYTES + (((C::KCHUNKS * ks + lk) ^ lds_swizzle<C::BK>(lr)) << 4));
+                (uint32_t)(lr * C::ROW_BYTES + (((C::KCHUNKS * ks + lk) ^ lds_swizzle<C::BK, C::MB>(lr)) << 4));
     }
 
     struct Frags {
