@@ -1535,29 +1535,52 @@ __device__ __forceinline__ void store_epilogue_wide(const TileCtx<C> &t, const t
     }
 }
 
-// bf16 D of the 8-wave barrier kernels, staged per wave: each wave turns one
-// 16-row block of its wave tile at a time around in a private LDS area of its
-// own (beside the ring, so the next tile's first stages can load meanwhile)
-// and stores it as whole rows. Lane l of a 16x16 block holds 4 consecutive
-// columns 4(l/16) .. +3 of row l%16; converted to bf16 (round to nearest
-// even, the same as a store would) they go to the wave's area row-major, then
-// each lane reads 16-byte chunks back eight to a row, and one store writes
-// 8 rows x WTN * 2 contiguous bytes. No workgroup barrier is needed: only the
-// wave itself uses its area, and a wave's LDS operations are performed in
-// order. Only rows < M and columns < N are written (the element-wise path for
-// a chunk that crosses column N or a row that is not 16-byte aligned).
+// bf16 D of the 16x16 barrier-hand-off kernels, staged per wave: each wave
+// turns one 16-row block of its wave tile at a time around in a private LDS
+// area of its own (beside the ring, so the next tile's first stages can load
+// meanwhile) and stores it as whole rows. Converted to bf16 (round to nearest
+// even, the same as a store would) and paired up across lanes (below), the
+// block row's columns go to the wave's area in 16-byte chunks; each lane then
+// reads 16-byte chunks back, WTN * 2 / 16 to a row, and one store writes
+// 64 / (WTN * 2 / 16) rows x WTN * 2 contiguous bytes. No workgroup barrier
+// is needed: only the wave itself uses its area, and a wave's LDS operations
+// are performed in order. Only rows < M and columns < N are written (the
+// element-wise path for a chunk that crosses column N or a row that is not
+// 16-byte aligned).
 template <class C>
 struct WaveEpilogue {
-    static constexpr int PITCH = C::WTN * 2 + 16;            // a staged row, padded
-    static constexpr int AREA = C::MB * PITCH;               // one wave's area
+    static constexpr int ROW_BYTES = C::WTN * 2;                // a staged row of bf16 D
+    static constexpr int AREA = C::MB * ROW_BYTES;              // one wave's area
     static constexpr int LDS_BYTES = C::WAVES * AREA;
-    static constexpr int CHUNKS_ROW = C::WTN * 2 / 16;       // 16-byte chunks per wave-tile row
-    static constexpr int ROWS = 64 / CHUNKS_ROW;             // rows per read (one chunk per lane)
-    static constexpr int READS = C::MB / ROWS;               // reads (and stores) per row block
+    static constexpr int CHUNKS_ROW = C::WTN * 2 / 16;          // 16-byte chunks per wave-tile row
+    static constexpr int ROWS = 64 / CHUNKS_ROW;                // rows per read (one chunk per lane)
+    static constexpr int READS = C::MB / ROWS;                  // reads (and stores) per row block
     static_assert(C::MB == 16 && C::OUT_BF16 && 64 % CHUNKS_ROW == 0 && C::MB % ROWS == 0, "wave-staged bf16 D");
+    static_assert(C::NI % 2 == 0 && CHUNKS_ROW == 2 * C::NI, "blocks staged in pairs");
     static_assert(C::MI * READS == C::BM * C::BN * 2 / 16 / C::THREADS, "every thread stores the same count");
+    // Chunk c of staged row r sits at position c ^ (r mod CHUNKS_ROW). With
+    // it both the 16-byte writes below (16 rows, one chunk per 16 lanes) and
+    // the 16-byte reads (ROWS rows, CHUNKS_ROW chunks each) measure
+    // conflict-free with the LDS bank conflict counter; a row pitch padded by
+    // 16 bytes, the usual remedy, leaves the reads at 4 conflict cycles each.
+    static __device__ __forceinline__ int pos(int r, int c) { return c ^ (r & (CHUNKS_ROW - 1)); }
 };
 
+// The bf16 bits of two fp32 values (round to nearest even), lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2 h;
+    h[0] = (__bf16)lo;
+    h[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// D of a full wave tile, staged per wave in 16-row slices through LDS and
+// stored as 16-byte chunks. A lane holds 4 consecutive columns of one row of
+// each 16x16 block (lane l: row l % 16, columns 4 (l / 16) ..): two
+// v_permlane16_swap per pair of neighbouring blocks give every lane 8
+// consecutive columns (16-lane group g: block ni + (g & 1), columns
+// 8 (g >> 1) ..), which it writes to LDS in one 16-byte store.
 template <class C>
 __device__ __forceinline__ void store_epilogue_wave(const TileCtx<C> &t, const typename C::Acc (&acc)[C::MI][C::NI],
                                                     int wm, int wn, int lane, int wave, uint8_t *area_base)
@@ -1565,7 +1588,7 @@ __device__ __forceinline__ void store_epilogue_wave(const TileCtx<C> &t, const t
     using E = WaveEpilogue<C>;
     lane = (int)opaque_v((uint32_t)lane);
     uint8_t *const area = area_base + wave * E::AREA;
-    const int lr = lane % 16, lc = (lane / 16) * 4;
+    const int lr = lane % 16, g = lane / 16;
     const int rr = lane / E::CHUNKS_ROW, cc = lane % E::CHUNKS_ROW; // this lane's chunk of a read
     const int row = wm * C::WTM + rr, col = wn * C::WTN + cc * 8;     // in the tile
     uint8_t *const base = (uint8_t *)t.d + ((int64_t)(t.row0 + row) * t.ldd + t.col0 + col) * 2;
@@ -1573,18 +1596,23 @@ __device__ __forceinline__ void store_epilogue_wave(const TileCtx<C> &t, const t
 #pragma unroll
     for (int mi = 0; mi < C::MI; ++mi) {
 #pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni) {
-            const typename C::Acc &v = acc[mi][ni];
-            bf16x4 h;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                h[e] = (__bf16)v[e];
-            *(bf16x4 *)(area + lr * E::PITCH + (ni * 16 + lc) * 2) = h;
+        for (int ni = 0; ni < C::NI; ni += 2) {
+            const typename C::Acc &x = acc[mi][ni], &y = acc[mi][ni + 1];
+            // groups 0..3 end up with columns 0-7 of x, 0-7 of y, 8-15 of x, 8-15 of y
+            const auto s0 = __builtin_amdgcn_permlane16_swap(pack_bf16x2(x[0], x[1]), pack_bf16x2(y[0], y[1]),
+                                                             false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(pack_bf16x2(x[2], x[3]), pack_bf16x2(y[2], y[3]),
+                                                             false, false);
+            const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
+            const int c = 2 * (ni + (g & 1)) + (g >> 1);
+            *(u32x4 *)(area + lr * E::ROW_BYTES + (E::pos(lr, c) << 4)) = w;
         }
         u32x4 chunk[E::READS];
 #pragma unroll
-        for (int j = 0; j < E::READS; ++j)
-            chunk[j] = *(const u32x4 *)(area + (j * E::ROWS + rr) * E::PITCH + cc * 16);
+        for (int j = 0; j < E::READS; ++j) {
+            const int r = j * E::ROWS + rr;
+            chunk[j] = *(const u32x4 *)(area + r * E::ROW_BYTES + (E::pos(r, cc) << 4));
+        }
 #pragma unroll
         for (int j = 0; j < E::READS; ++j) {
             uint8_t *const dst = base + ((int64_t)(mi * C::MB + j * E::ROWS) * t.ldd) * 2;
