@@ -150,6 +150,18 @@ __device__ __forceinline__ void dma_load16_if(uint32_t lds_addr, uint32_t voff, 
                  : "memory");
 }
 
+// The lanes of one wave exchange data through LDS here: each reads back what
+// other lanes wrote. The compiler models lanes as threads that do not see each
+// other's unsynchronized writes, so without this it may reuse a lane's earlier
+// load of an address the lane itself did not write in between (and it did,
+// moving reads into a branch only some lanes took). A wave performs its own
+// LDS operations in order, so no instruction is needed, only the compiler
+// barrier.
+__device__ __forceinline__ void wave_lds_exchange()
+{
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_address(const void *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;

@@ -984,7 +984,7 @@ struct Mainloop {
     // pre = the number of stores each thread issued after them when that is
     // exactly STORES (the previous tile was a full tile), else 0: the wait for
     // stage 0 then leaves stage 1's loads and those stores in flight.
-    static constexpr int STORES = C::BM * C::BN * 2 / 16 / C::THREADS; // 16-byte bf16 stores per thread
+    static constexpr int STORES = C::BM * C::BN * (C::OUT_BF16 ? 2 : 4) / 16 / C::THREADS; // 16-byte stores per thread
     template <bool FULL>
     __device__ __forceinline__ void first_stages(const TileCtx<C> &t, int pre)
     {
@@ -996,9 +996,16 @@ struct Mainloop {
             issue_any(0, 0, t.k, nk);
             wait_vmcnt<0>();
         } else if (pre == STORES && nk > 1) {
-            wait_vmcnt<STAGE_LOADS + STORES>();
+            // (kernels whose count does not fit the counter never pass pre > 0)
+            if constexpr (STAGE_LOADS + STORES <= 63)
+                wait_vmcnt<STAGE_LOADS + STORES>();
+            else
+                wait_vmcnt<0>();
         } else if (pre == STORES) {
-            wait_vmcnt<STORES>();
+            if constexpr (STORES <= 63)
+                wait_vmcnt<STORES>();
+            else
+                wait_vmcnt<0>();
         } else {
             wait_vmcnt<0>();
         }
@@ -1607,12 +1614,14 @@ __device__ __forceinline__ void store_epilogue_wave(const TileCtx<C> &t, const t
             const int c = 2 * (ni + (g & 1)) + (g >> 1);
             *(u32x4 *)(area + lr * E::ROW_BYTES + (E::pos(lr, c) << 4)) = w;
         }
+        wave_lds_exchange();
         u32x4 chunk[E::READS];
 #pragma unroll
         for (int j = 0; j < E::READS; ++j) {
             const int r = j * E::ROWS + rr;
             chunk[j] = *(const u32x4 *)(area + r * E::ROW_BYTES + (E::pos(r, cc) << 4));
         }
+        wave_lds_exchange();
 #pragma unroll
         for (int j = 0; j < E::READS; ++j) {
             uint8_t *const dst = base + ((int64_t)(mi * C::MB + j * E::ROWS) * t.ldd) * 2;
@@ -1635,13 +1644,94 @@ __device__ __forceinline__ void store_epilogue_wave(const TileCtx<C> &t, const t
     }
 }
 
+// fp32 D of the 8-wave 16x16 barrier-hand-off kernels, staged per wave like
+// bf16 D above, in 8-row halves of each 16-row block (a whole fp32 block row
+// per wave beside the ring would need all 160 KiB of LDS). A lane's 4 fp32
+// of a block are one 16-byte chunk already; the lanes of the half's rows write
+// them, then every lane reads 16-byte chunks back, WTN * 4 / 16 to a row.
+// Chunk c of staged row r sits at c ^ (r mod chunks per row): with it the
+// half-wave 16-byte writes and the 16-byte reads both measure conflict-free
+// with the LDS bank conflict counter. Only rows < M and columns < N are
+// written.
+template <class C>
+struct WaveEpilogueF32 {
+    static constexpr int ROW_BYTES = C::WTN * 4;                // a staged row of fp32 D
+    static constexpr int HALF = C::MB / 2;                      // rows staged at a time
+    static constexpr int AREA = HALF * ROW_BYTES;               // one wave's area
+    static constexpr int LDS_BYTES = C::WAVES * AREA;
+    static constexpr int CHUNKS_ROW = C::WTN * 4 / 16;          // 16-byte chunks per wave-tile row
+    static constexpr int ROWS = 64 / CHUNKS_ROW;                // rows per read (one chunk per lane)
+    static constexpr int READS = HALF / ROWS;                   // reads (and stores) per half
+    static_assert(C::MB == 16 && !C::OUT_BF16 && 64 % CHUNKS_ROW == 0 && HALF % ROWS == 0, "wave-staged fp32 D");
+    static_assert(CHUNKS_ROW == 4 * C::NI, "a lane's block chunk: 4 per 16x16 block row");
+    static_assert(C::MI * 2 * READS == C::BM * C::BN * 4 / 16 / C::THREADS, "every thread stores the same count");
+    static __device__ __forceinline__ int pos(int r, int c) { return c ^ (r & (CHUNKS_ROW - 1)); }
+};
+
+template <class C>
+__device__ __forceinline__ void store_epilogue_wave_f32(const TileCtx<C> &t,
+                                                        const typename C::Acc (&acc)[C::MI][C::NI], int wm, int wn,
+                                                        int lane, int wave, uint8_t *area_base)
+{
+    using E = WaveEpilogueF32<C>;
+    lane = (int)opaque_v((uint32_t)lane);
+    uint8_t *const area = area_base + wave * E::AREA;
+    const int lr = lane % 16, g = lane / 16;
+    const int rr = lane / E::CHUNKS_ROW, cc = lane % E::CHUNKS_ROW; // this lane's chunk of a read
+    const int row = wm * C::WTM + rr, col = wn * C::WTN + cc * 4;     // in the tile
+    uint8_t *const base = (uint8_t *)t.d + ((int64_t)(t.row0 + row) * t.ldd + t.col0 + col) * 4;
+    const bool full = t.vec_ok && t.vm == C::BM && t.vn == C::BN;
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (lr / E::HALF == h) {
+                const int sr = lr % E::HALF;
+#pragma unroll
+                for (int ni = 0; ni < C::NI; ++ni)
+                    *(f32x4 *)(area + sr * E::ROW_BYTES + (E::pos(sr, 4 * ni + g) << 4)) = acc[mi][ni];
+            }
+            wave_lds_exchange();
+            f32x4 chunk[E::READS];
+#pragma unroll
+            for (int j = 0; j < E::READS; ++j) {
+                const int r = j * E::ROWS + rr;
+                chunk[j] = *(const f32x4 *)(area + r * E::ROW_BYTES + (E::pos(r, cc) << 4));
+            }
+            wave_lds_exchange();
+#pragma unroll
+            for (int j = 0; j < E::READS; ++j) {
+                const int dr = mi * C::MB + h * E::HALF + j * E::ROWS;   // row offset from `row`
+                uint8_t *const dst = base + ((int64_t)dr * t.ldd) * 4;
+                if (full) {
+                    __builtin_nontemporal_store(chunk[j], (f32x4 *)dst);
+                } else {
+                    const int i = row + dr;
+                    if (i < t.vm && col < t.vn) {
+                        if (t.vec_ok && col + 4 <= t.vn) {
+                            __builtin_nontemporal_store(chunk[j], (f32x4 *)dst);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (col + e < t.vn)
+                                    ((float *)dst)[e] = chunk[j][e];
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <class C, bool USED>
 constexpr int wave_epilogue_lds_bytes()
 {
-    if constexpr (USED)
+    if constexpr (!USED)
+        return 0;
+    else if constexpr (C::OUT_BF16)
         return WaveEpilogue<C>::LDS_BYTES;
     else
-        return 0;
+        return WaveEpilogueF32<C>::LDS_BYTES;
 }
 
 template <class C, bool WIDE>
@@ -1667,10 +1757,12 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
     // the two-waves-per-SIMD 16x16 kernels stage bf16 D as bf16 (WideEpilogue);
     // with the barrier hand-off they, and the one-wave-per-SIMD 16x16 kernel,
     // stage it per wave, beside the ring, and load the next tile's first
-    // stages during the epilogue (WaveEpilogue)
+    // stages during the epilogue (WaveEpilogue; fp32 D of the two-wave ones
+    // in half blocks, WaveEpilogueF32)
     constexpr bool WIDE_EPI = C::WAVES == 8 && C::MB == 16 && C::OUT_BF16;
     constexpr bool SINGLE_EPI = C::WAVES == 4 && C::MB == 16 && C::OUT_BF16;
-    constexpr bool PREFETCH = (WIDE_EPI || SINGLE_EPI) && C::SYNC == SYNC_BARRIER;
+    constexpr bool F32_EPI = C::WAVES == 8 && C::MB == 16 && !C::OUT_BF16;
+    constexpr bool PREFETCH = (WIDE_EPI || SINGLE_EPI || F32_EPI) && C::SYNC == SYNC_BARRIER;
     constexpr int EPI_BYTES = PREFETCH ? 0 : epilogue_lds_bytes<C, WIDE_EPI>();
     constexpr int WAVE_EPI_BYTES = wave_epilogue_lds_bytes<C, PREFETCH>();
     constexpr int SMEM_BYTES = (C::LDS_BYTES > EPI_BYTES ? C::LDS_BYTES : EPI_BYTES) + WAVE_EPI_BYTES;
@@ -1753,7 +1845,10 @@ void gemm_persistent_kernel(const GemmArgs args_by_value)
                 ml.setup(tn);
                 ml.issue_first_two(tn);
             }
-            store_epilogue_wave<C>(tc, acc, ml.wm, ml.wn, (int)lane_id(), wave, smem + C::LDS_BYTES);
+            if constexpr (C::OUT_BF16)
+                store_epilogue_wave<C>(tc, acc, ml.wm, ml.wn, (int)lane_id(), wave, smem + C::LDS_BYTES);
+            else
+                store_epilogue_wave_f32<C>(tc, acc, ml.wm, ml.wn, (int)lane_id(), wave, smem + C::LDS_BYTES);
             pre = (tc.vec_ok && tc.vm == C::BM && tc.vn == C::BN) ? Mainloop<C>::STORES : 0;
             if (tracing && leader) {
                 TileTrace r;

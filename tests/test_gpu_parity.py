@@ -262,23 +262,27 @@ def test_tile_reuse_does_not_accumulate_across_tiles(pts):
         U.check_exact(d, ref, f"single worker {sched}")
 
 
-@pytest.mark.parametrize("tile", [(256, 256, 64, 2, 1, 8, 16), (256, 256, 64, 2, 1, 4, 16)])
-def test_few_workers_many_tiles_bf16(pts, tile):
-    # Five workers take 72 tiles (full and edge ones in turn, a partial last
-    # k-tile, k order rotated past the first 32 positions) with bf16 output:
-    # the tile loop that issues each next tile's first two stages before this
-    # tile's stores and then waits for the first stage only, on both 256x256
-    # 16x16 kernels, every schedule that takes a worker count.
+@pytest.mark.parametrize("tile,out_dtype", [((256, 256, 64, 2, 1, 8, 16), torch.bfloat16),
+                                            ((256, 256, 64, 2, 1, 4, 16), torch.bfloat16),
+                                            ((256, 256, 64, 2, 1, 8, 16), torch.float32),
+                                            ((256, 128, 64, 2, 1, 8, 16), torch.float32)])
+def test_few_workers_many_tiles(pts, tile, out_dtype):
+    # Five workers take many tiles (full and edge ones in turn, a partial last
+    # k-tile, k order rotated past the first 32 positions): the tile loop that
+    # issues each next tile's first two stages before this tile's stores and
+    # then waits for the first stage only, on the 16x16 kernels that run it
+    # (bf16 output on both 256x256 kernels, fp32 output on the two-wave ones),
+    # every schedule that takes a worker count.
     m, n, k = 1800, 2100, 1000
     lda = ldb = _padded_ld(k)
     a_bits, b_bits = _operands(m, n, k, 17, kind="integer", lda=lda, ldb=ldb)
     ref = oracle.gemm(a_bits, b_bits, m, n, k, lda=lda, ldb=ldb)
     a, b = U.bits_to_device(a_bits), U.bits_to_device(b_bits)
     for sched in PERSISTENT:
-        U.log(f"few workers, many tiles: tile {tile} {sched}")
-        d, counters, (tiles, workers) = U.run_single(m, n, k, a, b, torch.bfloat16, sched, tile=tile, lda=lda,
+        U.log(f"few workers, many tiles: tile {tile} {out_dtype} {sched}")
+        d, counters, (tiles, workers) = U.run_single(m, n, k, a, b, out_dtype, sched, tile=tile, lda=lda,
                                                      ldb=ldb, num_workers=5)
-        assert (tiles, workers) == (72, 5)
+        assert (tiles, workers) == ((72 if tile[1] == 256 else 136), 5)
         U.check_exact(d[:m, :n], ref, f"5 workers tile {tile} {sched}")
         U.check_counters(sched, counters, tiles, workers)
 
