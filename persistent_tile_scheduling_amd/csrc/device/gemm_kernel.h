@@ -339,6 +339,19 @@ __device__ __forceinline__ TileCtx<C> decode_tile(KernArgs args, int t, int grou
     return c;
 }
 
+// The order of a k-step's MFMAs over its MI x NI blocks: rows in turn, each
+// row's columns ascending on even rows and descending on odd ones, so every
+// MFMA shares an operand with the one before it (the row's A fragment inside
+// a row, the last column's B fragment across a row change). Under the power
+// limit that is worth about 2% of clock against rows all walked the same way
+// (measured on an MFMA-only stream of this kernel's shape; with no operand
+// shared between neighbours, 3% less again).
+template <int NI>
+__device__ __forceinline__ constexpr int serpentine_col_of(int mi, int nn)
+{
+    return (mi & 1) ? NI - 1 - nn : nn;
+}
+
 template <class C>
 struct Mainloop {
     uint8_t *smem;
@@ -374,6 +387,10 @@ struct Mainloop {
     // holds k-tile phys(kt). Every k offset and every "is this the partial
     // last k-tile" test goes through it.
     int kt0, nk_all;
+    static __device__ __forceinline__ constexpr int serpentine_col(int mi, int nn)
+    {
+        return serpentine_col_of<C::NI>(mi, nn);
+    }
     __device__ __forceinline__ int phys(int kt) const
     {
         const int p = kt + kt0;
@@ -791,9 +808,11 @@ struct Mainloop {
         for (int mi = 0; mi < C::MI; ++mi) {
             const bool spare_row = mi >= C::MI - SP;
 #pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
+            for (int nn = 0; nn < C::NI; ++nn) {
+                const int ni = serpentine_col(mi, nn);
                 acc[mi][ni] = C::Op::run(f.b[BS][ni], (BS == 1 && spare_row) ? f.ax[mi - (C::MI - SP)] : f.a[mi],
                                          acc[mi][ni]);
+            }
             if (!spare_row)
                 f.a[mi] = *(const bf16x8 *)(sa + frag_off[ks] + mi * C::MB * C::ROW_BYTES);
             if (mi < C::NI)
@@ -1115,7 +1134,7 @@ struct Mainloop {
         const uint32_t foff = frag_off[rks];
 #pragma unroll
         for (int x = 0; x < S_MFMAS; ++x) {
-            const int mi = x / C::NI, ni = x % C::NI;
+            const int mi = x / C::NI, ni = serpentine_col(mi, x % C::NI);
             C::Op::run_fixed(cur.b[ni], cur.a[mi], acc[mi][ni]);
             if (x % READ_EVERY == 0 && x / READ_EVERY < S_READS)
                 read_frag(nxt, x / READ_EVERY, sa, sb, foff);
@@ -1140,7 +1159,7 @@ struct Mainloop {
         const uint32_t foff = frag_off[rks];
 #pragma unroll
         for (int x = 0; x < S_MFMAS; ++x) {
-            const int mi = x / C::NI, ni = x % C::NI;
+            const int mi = x / C::NI, ni = serpentine_col(mi, x % C::NI);
             C::Op::run_fixed(cur.b[ni], cur.a[mi], acc[mi][ni]);
             if (x % READ_EVERY == 0 && x / READ_EVERY < S_READS)
                 read_frag(nxt, x / READ_EVERY, sa, sb, foff);
