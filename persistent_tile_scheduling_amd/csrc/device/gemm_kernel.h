@@ -594,8 +594,10 @@ struct Mainloop {
 #pragma unroll
         for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
+            for (int nn = 0; nn < C::NI; ++nn) {
+                const int ni = serpentine_col(mi, nn);
                 acc[mi][ni] = C::Op::run(f.b[ni], f.a[mi], acc[mi][ni]);
+            }
     }
 
     // Ask the scheduler to interleave the next k-step's fragment reads with
