@@ -332,8 +332,12 @@ def test_grouped_small_full_oracle(pts):
             assert torch.equal(x.nan_to_num(0.0), y.nan_to_num(0.0))
 
 
-def test_grouped_variable_k_full_oracle(pts):
-    # per-problem K (tiles of unequal cost), ragged M, N and K, fp32 out
+@pytest.mark.parametrize("out_dtype,num_workers", [(torch.float32, 0), (torch.float32, 3), (torch.bfloat16, 3)])
+def test_grouped_variable_k_full_oracle(pts, out_dtype, num_workers):
+    # per-problem K (tiles of unequal cost), ragged M, N and K, a K = 0 and a
+    # K = 1 problem; with 3 workers the tiles of every K follow each other on a
+    # worker, so a tile with no k-tile (nothing loaded, only stores) sits
+    # between tiles whose first stages load during the previous epilogue
     rng = np.random.default_rng(6)
     shapes = [(int(rng.integers(1, 400)), int(rng.integers(1, 400)), int(rng.integers(1, 40)) * 8 + int(rng.integers(0, 8)))
               for _ in range(9)] + [(300, 200, 0), (257, 129, 1)]
@@ -345,21 +349,21 @@ def test_grouped_variable_k_full_oracle(pts):
         b_bits = gen.operand_b(k, n, 2, tensor_id=tb, ldb=ld)
         refs.append(oracle.gemm(a_bits, b_bits, m, n, k, lda=ld, ldb=ld))
         tensors.append((U.bits_to_device(a_bits), U.bits_to_device(b_bits),
-                        torch.full((m, n), float("nan"), dtype=torch.float32, device=U.DEV)))
+                        torch.full((m, n), float("nan"), dtype=out_dtype, device=U.DEV)))
     plan_shapes = [(m, n, k, _padded_ld(k), _padded_ld(k), 0) for (m, n, k) in shapes]
     outs = {}
-    for sched in SCHEDULES:
-        U.log(f"grouped variable K {sched}")
+    for sched in (SCHEDULES if num_workers == 0 else PERSISTENT):
+        U.log(f"grouped variable K {sched} {out_dtype} workers {num_workers}")
         for (_, _, d) in tensors:
             d.fill_(float("nan"))
-        with pts.Plan(plan_shapes, torch.float32, schedule=sched) as p:
+        with pts.Plan(plan_shapes, out_dtype, schedule=sched, num_workers=num_workers) as p:
             p.run(tensors)
             torch.cuda.synchronize()
             U.check_counters(sched, p.counters(), p.num_tiles, p.num_workers)
         for g, ((m, n, k), (_, _, d)) in enumerate(zip(shapes, tensors)):
             U.check_close(d, refs[g], max(k, 1), f"group {g} {(m, n, k)} {sched}")
         outs[sched] = [d.clone() for (_, _, d) in tensors]
-    for sched in SCHEDULES[1:]:
+    for sched in list(outs)[1:]:
         for x, y in zip(outs["static"], outs[sched]):
             assert torch.equal(x, y)
 
