@@ -233,7 +233,10 @@ gemm_status gemm_plan_create(const gemm_desc *desc, gemm_plan **out_plan);
  * Scheduling" and "Scheduling Shapes"), the tile body being the GEMM
  * mainloop of "Pipeline Groups", section "Overview". `ops` is a host array of desc.group_count operand sets.
  * Returns GEMM_ERR_INVALID_VALUE for a NULL or misaligned pointer (nothing is
- * launched), GEMM_ERR_HIP if the launch fails. Problems with m = 0 or n = 0
+ * launched), GEMM_ERR_HIP if the launch fails. No element of any problem's D
+ * may lie in another problem's D or in any problem's A or B (D blocks may
+ * interleave inside one wider matrix, as column blocks do); overlapping
+ * operands are not detected and give undefined results. Problems with m = 0 or n = 0
  * write nothing; k = 0 writes zeros. The run must be on the device the plan
  * was created on. The call enqueues that one kernel and nothing else (no
  * memset, copy or host synchronisation; the dynamic schedules' claim counters

@@ -334,7 +334,8 @@ def gemm(a: torch.Tensor, b: torch.Tensor, out_dtype=torch.float32, schedule="st
     must be a multiple of 8 elements, ``stride(1)`` must be 1 and the first
     element 16-byte aligned. ``k``
     defaults to ``a.shape[1]``. ``out`` (fp32 or bf16, m x n, ``stride(1) == 1``)
-    is written in place when given. Every tensor must be on the current GPU.
+    is written in place when given and must not share memory with ``a`` or ``b``
+    (not checked). Every tensor must be on the current GPU.
     Anything else raises ``ValueError``. Builds a one-shot plan; the tile
     defaults to the library's choice for the sizes ("auto").
     """
