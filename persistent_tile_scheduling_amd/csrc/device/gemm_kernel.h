@@ -50,7 +50,7 @@ struct GroupDesc {
     int32_t tile_begin;  // index of the problem's first tile in the run's tile space
     int32_t num_k_tiles; // ceil(k / BK)
     int32_t index;       // the problem's index in the plan descriptor (tile order may differ)
-    int32_t pad1;
+    int32_t band_rows;   // tile rows per band of the tile order (raster_tile)
     int64_t lda, ldb, ldd;
 };
 
@@ -244,21 +244,39 @@ __device__ __forceinline__ KernArgs kernel_args()
     return (KernArgs)__builtin_amdgcn_kernarg_segment_ptr();
 }
 
-// Tile order inside one problem: the tile rows are taken in groups of
-// RASTER_ROWS, and each group is walked column by column, so any run of
-// consecutive positions covers a compact block (8 consecutive positions: one
-// column of 8 tiles; 32: 8 x 4 tiles) whose A and B panels are few and shared.
-// This is an order, not a change of work: every tile has exactly one position.
+// Tile order inside one problem, in three levels:
+//   * a block: RASTER_ROWS tile rows by RASTER_COLS tile columns, walked
+//     column by column (32 consecutive positions, what one die's workers run
+//     in one round of the static dealing: a compact block whose A and B
+//     panels that die's L2 shares);
+//   * a stripe: RASTER_COLS columns of a band of `band` tile rows, its
+//     blocks one below the other;
+//   * a band: `band` tile rows (a multiple of RASTER_ROWS), its stripes left
+//     to right.
+// With band = RASTER_ROWS a stripe is one block and a band is walked column
+// by column. A problem whose B does not fit the memory-side cache takes wider
+// bands (the plan sets `band` per problem): successive rounds then walk along
+// one band, whose A panels every round of it reads again while each B panel
+// is needed by one round only, so the A band stays cached and B streams past
+// once per band instead of once per group of RASTER_ROWS rows. Partial
+// bands, stripes and blocks at the edges keep the same order. This is an
+// order, not a change of work: every tile has exactly one position.
 constexpr int RASTER_ROWS = 8;
+constexpr int RASTER_COLS = 4;
 
-__device__ __forceinline__ void raster_tile(int local, int tiles_m, int tiles_n, int &tm, int &tn)
+__device__ __forceinline__ void raster_tile(int local, int tiles_m, int tiles_n, int band, int &tm, int &tn)
 {
-    const int group = local / (RASTER_ROWS * tiles_n);
-    const int first_row = group * RASTER_ROWS;
-    const int rows = min(RASTER_ROWS, tiles_m - first_row);
-    const int within = local - first_row * tiles_n;
-    tm = first_row + within % rows;
-    tn = within / rows;
+    const int first_row = local / (band * tiles_n) * band;
+    const int band_rows = min(band, tiles_m - first_row);
+    const int in_band = local - first_row * tiles_n;
+    const int stripe = in_band / (band_rows * RASTER_COLS);
+    const int stripe_cols = min(RASTER_COLS, tiles_n - stripe * RASTER_COLS);
+    const int in_stripe = in_band - stripe * band_rows * RASTER_COLS;
+    const int block = in_stripe / (RASTER_ROWS * stripe_cols);
+    const int block_rows = min(RASTER_ROWS, band_rows - block * RASTER_ROWS);
+    const int in_block = in_stripe - block * RASTER_ROWS * stripe_cols;
+    tm = first_row + block * RASTER_ROWS + in_block % block_rows;
+    tn = stripe * RASTER_COLS + in_block / block_rows;
 }
 
 // Where a tile's k loop starts. Each compute die (XCD) works on a compact
@@ -318,7 +336,7 @@ __device__ __forceinline__ TileCtx<C> decode_tile(KernArgs args, int t, int grou
     gd.ldd = gp->ldd;
     const int local = t - gd.tile_begin;
     int tm, tn;
-    raster_tile(local, (gd.m + C::BM - 1) / C::BM, gd.tiles_n, tm, tn);
+    raster_tile(local, (gd.m + C::BM - 1) / C::BM, gd.tiles_n, gp->band_rows, tm, tn);
     TileCtx<C> c;
     c.group = g;
     c.problem = gp->index;

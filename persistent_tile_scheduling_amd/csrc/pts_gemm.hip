@@ -145,6 +145,19 @@ void pick_auto_tile(const gemm_desc *desc, int cus, int &tm, int &tn)
     tm = tn = 64;
 }
 
+// Tile rows per band of a problem's tile order (the device's raster_tile). A
+// band of RASTER_ROWS rows walks every column for each group of 8 tile rows,
+// so B is read again per group unless the memory-side cache (256 MiB on
+// MI355X, shared by the dies) keeps it: when B takes more than half of that
+// cache the order uses bands of 32 tile rows, whose A panels stay cached
+// while B streams past once per band (16384 x 16384 x 8192: +5%). Otherwise
+// the narrow band (measured 0.5-0.9% better where everything fits).
+constexpr int64_t WIDE_BAND_B_BYTES = (int64_t)128 << 20;
+static int32_t band_rows_for(const gemm_shape &s)
+{
+    return (int64_t)s.n * s.k * 2 > WIDE_BAND_B_BYTES ? 32 : 8;
+}
+
 // Validate a descriptor and lay out its tile space (the plan's host part).
 // Allocates no device memory; needs the current HIP device for the compute
 // unit count and the kernel's occupancy.
@@ -257,7 +270,7 @@ gemm_status build_core(const gemm_desc *desc, PlanCore &core)
         gd.tile_begin = 0;
         gd.num_k_tiles = (int32_t)ceil_div(s.k, entry->bk);
         gd.index = g;
-        gd.pad1 = 0;
+        gd.band_rows = band_rows_for(s);
         gd.lda = s.lda;
         gd.ldb = s.ldb;
         gd.ldd = s.ldd;

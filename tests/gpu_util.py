@@ -159,3 +159,25 @@ def check_against_fp32_matmul(d: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
         worst = max(worst, err)
     assert worst <= tol, f"{what}: max |D - fp32 ref| = {worst:.3g} > {tol:.3g}"
     return worst
+
+
+def band_rows(n, k):
+    """Tile rows per band of the plan's tile order: 32 when B (n x k bf16)
+    takes more than 128 MiB, else 8."""
+    return 32 if n * k * 2 > (128 << 20) else 8
+
+
+def raster_tile(pos, tiles_m, tiles_n, band, rows=8, cols=4):
+    """The plan's tile order inside one problem: bands of `band` tile rows,
+    each walked in stripes of `cols` columns, each stripe in blocks of `rows`
+    rows walked column by column: position -> (tile row, tile column)."""
+    first = pos // (band * tiles_n) * band
+    rows_in_band = min(band, tiles_m - first)
+    in_band = pos - first * tiles_n
+    stripe = in_band // (rows_in_band * cols)
+    stripe_cols = min(cols, tiles_n - stripe * cols)
+    in_stripe = in_band - stripe * rows_in_band * cols
+    block = in_stripe // (rows * stripe_cols)
+    block_rows = min(rows, rows_in_band - block * rows)
+    in_block = in_stripe - block * rows * stripe_cols
+    return first + block * rows + in_block % block_rows, stripe * cols + in_block // block_rows

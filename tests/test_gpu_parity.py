@@ -475,16 +475,6 @@ def test_config4_grouped_64_problems_whole_tiles(pts):
     assert full_tiles >= sum(1 for m in ms if m >= bm)
 
 
-def _raster_tile(pos, tiles_m, tiles_n, rows=8):
-    """The plan's tile order inside one problem (groups of `rows` tile rows,
-    each walked column by column): position -> (tile row, tile column)."""
-    group = pos // (rows * tiles_n)
-    first = group * rows
-    nrows = min(rows, tiles_m - first)
-    within = pos - first * tiles_n
-    return first + within % nrows, within // nrows
-
-
 @pytest.mark.timeout(600)
 def test_config5_with_concurrent_copy_whole_tiles(pts):
     """16384^2 x 8192 while an int16 copy holds 64 CUs. 64 whole tiles are
@@ -529,7 +519,7 @@ def test_config5_with_concurrent_copy_whole_tiles(pts):
         for s in range(8):
             pos = 32 * (8 * ((3 * s + c) % 16) + c) + (5 * s + c) % 32
             classes.add((pos // 32) % 8)
-            tm, tn = _raster_tile(pos, tiles_m, tiles_n)
+            tm, tn = U.raster_tile(pos, tiles_m, tiles_n, U.band_rows(n, k))
             blocks.append((tm * bm, tm * bm + bm, tn * bn, tn * bn + bn))
     assert classes == set(range(8)) and len(set(blocks)) == 64
     U.log(f"  oracle: 64 whole tiles of 256x256x{k}")

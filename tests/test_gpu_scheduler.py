@@ -171,6 +171,20 @@ def _traced_run(pts, shapes, schedule, tile=(0, 0), num_workers=0, out_dtype=tor
         return tiles.copy(), workers.copy(), p.num_tiles, p.num_workers, p.counters()
 
 
+@pytest.mark.parametrize("m,n,k", [(9000, 8200, 8200), (5000, 7000, 64)])
+def test_tile_order_bands(pts, m, n, k):
+    """The kernel's position -> tile map, read from its trace, is the banded
+    order: 32-row bands where B (n x k bf16) exceeds 128 MiB (here with a
+    partial last band and a ragged last stripe), 8-row bands otherwise."""
+    U.log(f"tile order: {m} x {n} x {k}, band {U.band_rows(n, k)}")
+    tiles, _, nt, _, _ = _traced_run(pts, [(m, n)], "static", (256, 256), k=k)
+    tiles_m, tiles_n = -(-m // 256), -(-n // 256)
+    assert nt == tiles_m * tiles_n
+    band = U.band_rows(n, k)
+    for pos, r0, c0 in zip(tiles["tile"].tolist(), tiles["row0"].tolist(), tiles["col0"].tolist()):
+        assert (r0 // 256, c0 // 256) == U.raster_tile(pos, tiles_m, tiles_n, band), f"position {pos}"
+
+
 @pytest.mark.parametrize("schedule", ["static", "dynamic", "dynamic_xcd", "nonpersistent"])
 @pytest.mark.parametrize("shapes,tile", [([(5000, 7000)], (256, 256)), ([(256, 256)], (64, 64)),
                                          ([(300, 200), (0, 10), (1000, 64), (1, 1)], (128, 128)),
