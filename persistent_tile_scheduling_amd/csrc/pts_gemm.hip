@@ -146,16 +146,22 @@ void pick_auto_tile(const gemm_desc *desc, int cus, int &tm, int &tn)
 }
 
 // Tile rows per band of a problem's tile order (the device's raster_tile). A
-// band of RASTER_ROWS rows walks every column for each group of 8 tile rows,
-// so B is read again per group unless the memory-side cache (256 MiB on
-// MI355X, shared by the dies) keeps it: when B takes more than half of that
-// cache the order uses bands of 32 tile rows, whose A panels stay cached
-// while B streams past once per band (16384 x 16384 x 8192: +5%). Otherwise
-// the narrow band (measured 0.5-0.9% better where everything fits).
+// band of 8 tile rows walks every column for each group of 8 tile rows, so B
+// is read again per group unless the memory-side cache (256 MiB on MI355X,
+// shared by the dies) keeps it. When B takes more than half of that cache the
+// band widens to the most tile rows, a multiple of 8 up to 64, whose A panels
+// fit in three quarters of it: they stay cached while B streams past once per
+// band. At 16384 x 16384 x 8192 (48 rows): +6.5%; 32 rows +5%, 24 +4%, 16
+// +1.5%, 64 (A band 256 MiB) +1.5%. Where B fits, the narrow band (0.5-0.9%
+// better there).
 constexpr int64_t WIDE_BAND_B_BYTES = (int64_t)128 << 20;
-static int32_t band_rows_for(const gemm_shape &s)
+constexpr int64_t BAND_A_BYTES = (int64_t)192 << 20;
+static int32_t band_rows_for(const gemm_shape &s, int tile_m)
 {
-    return (int64_t)s.n * s.k * 2 > WIDE_BAND_B_BYTES ? 32 : 8;
+    if ((int64_t)s.n * s.k * 2 <= WIDE_BAND_B_BYTES || s.k == 0)
+        return 8;
+    const int64_t rows = BAND_A_BYTES / ((int64_t)tile_m * s.k * 2) / 8 * 8;
+    return (int32_t)std::min<int64_t>(64, std::max<int64_t>(8, rows));
 }
 
 // Validate a descriptor and lay out its tile space (the plan's host part).
@@ -270,7 +276,7 @@ gemm_status build_core(const gemm_desc *desc, PlanCore &core)
         gd.tile_begin = 0;
         gd.num_k_tiles = (int32_t)ceil_div(s.k, entry->bk);
         gd.index = g;
-        gd.band_rows = band_rows_for(s);
+        gd.band_rows = band_rows_for(s, tm);
         gd.lda = s.lda;
         gd.ldb = s.ldb;
         gd.ldd = s.ldd;

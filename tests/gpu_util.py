@@ -161,10 +161,13 @@ def check_against_fp32_matmul(d: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
     return worst
 
 
-def band_rows(n, k):
-    """Tile rows per band of the plan's tile order: 32 when B (n x k bf16)
-    takes more than 128 MiB, else 8."""
-    return 32 if n * k * 2 > (128 << 20) else 8
+def band_rows(n, k, bm=256):
+    """Tile rows per band of the plan's tile order: 8, or where B (n x k bf16)
+    takes more than 128 MiB, the most tile rows (a multiple of 8 from 8 to 64)
+    whose A rows (bm x k bf16 per tile row) fit in 192 MiB."""
+    if n * k * 2 <= (128 << 20) or k == 0:
+        return 8
+    return min(64, max(8, (192 << 20) // (bm * k * 2) // 8 * 8))
 
 
 def raster_tile(pos, tiles_m, tiles_n, band, rows=8, cols=4):

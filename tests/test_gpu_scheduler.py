@@ -171,11 +171,12 @@ def _traced_run(pts, shapes, schedule, tile=(0, 0), num_workers=0, out_dtype=tor
         return tiles.copy(), workers.copy(), p.num_tiles, p.num_workers, p.counters()
 
 
-@pytest.mark.parametrize("m,n,k", [(9000, 8200, 8200), (5000, 7000, 64)])
+@pytest.mark.parametrize("m,n,k", [(13000, 8200, 8200), (5000, 7000, 64)])
 def test_tile_order_bands(pts, m, n, k):
     """The kernel's position -> tile map, read from its trace, is the banded
-    order: 32-row bands where B (n x k bf16) exceeds 128 MiB (here with a
-    partial last band and a ragged last stripe), 8-row bands otherwise."""
+    order: wide bands where B (n x k bf16) exceeds 128 MiB (here 40 rows, with
+    a partial last band, a partial last block and a ragged last stripe), 8-row
+    bands otherwise."""
     U.log(f"tile order: {m} x {n} x {k}, band {U.band_rows(n, k)}")
     tiles, _, nt, _, _ = _traced_run(pts, [(m, n)], "static", (256, 256), k=k)
     tiles_m, tiles_n = -(-m // 256), -(-n // 256)
